@@ -1,0 +1,81 @@
+"""Single-element evaluation of the collectives (test infrastructure only).
+
+At full workload sizes the step-by-step emulation in `collectives` does not fit
+in host memory, but every output element of a reduction depends only on the N
+inputs at one position, and every output row of a permutation comes from one
+input row.  These functions evaluate chosen output positions directly from the
+fold order the ring induces (DTLM §2 "Reduce-Scatter": chunk j is folded
+starting at rank j+1 and ends at its owner j), and the tests pin them to the
+step-by-step emulation on sizes where both run.
+"""
+
+import numpy as np
+
+from .collectives import _epilogue, _widen, a2a_recv_offsets, a2a_send_offsets
+
+
+def fold_start(positions, S, N, order, chunk=None):
+    """First rank of the fold for each element position (ring: owner + 1; rank: 0)."""
+    positions = np.asarray(positions, dtype=np.int64)
+    if order == "rank":
+        return np.zeros(positions.shape, dtype=np.int64)
+    c = chunk if chunk is not None else (-(-S // N) if S else 1)
+    owner = positions // c
+    return (owner + 1) % N
+
+
+def reduce_positions(values, dtype, starts, op, out_dtype):
+    """values[i][k] = rank i's input at the k-th sampled position; fold in the given rank order.
+
+    Element k is folded as values[start_k], values[start_k + 1], ... (mod N),
+    starting from the first term, then averaged and cast like the owner does.
+    """
+    values = np.asarray(values)
+    N, m = values.shape
+    wide = np.stack([_widen(values[i], dtype) for i in range(N)])
+    cols = np.arange(m)
+    starts = np.asarray(starts, dtype=np.int64)
+    acc = wide[starts % N, cols].copy()
+    with np.errstate(over="ignore", invalid="ignore"):
+        for t in range(1, N):
+            acc = acc + wide[(starts + t) % N, cols]
+    return _epilogue(acc, op, N, out_dtype)
+
+
+def all_reduce_at(values, positions, S, dtype, op, order):
+    """All-reduce outputs at the sampled positions (same value on every rank)."""
+    N = np.asarray(values).shape[0]
+    return reduce_positions(values, dtype, fold_start(positions, S, N, order), op, dtype)
+
+
+def reduce_scatter_at(values, owner, out_pos, recv_count, in_dtype, out_dtype, op, order):
+    """Reduce-scatter output recv[owner][out_pos]; values[i][k] = send[i][owner*recv_count + out_pos]."""
+    N = np.asarray(values).shape[0]
+    owner = np.asarray(owner, dtype=np.int64)
+    starts = (owner + 1) % N if order == "ring" else np.zeros_like(owner)
+    return reduce_positions(values, in_dtype, starts, op, out_dtype)
+
+
+def a2a_source_rows(splits, d, recv_rows):
+    """For rows of rank d's receive buffer, the (source rank, source row) they come from."""
+    splits = np.asarray(splits, dtype=np.int64)
+    N, _, E = splits.shape
+    soff = a2a_send_offsets(splits)
+    roff = a2a_recv_offsets(splits)
+    out_s = np.empty(len(recv_rows), dtype=np.int64)
+    out_row = np.empty(len(recv_rows), dtype=np.int64)
+    for k, row in enumerate(np.asarray(recv_rows, dtype=np.int64)):
+        found = False
+        for e in range(E):
+            for s in range(N):
+                lo = roff[s, d, e]
+                if lo <= row < lo + splits[s, d, e]:
+                    out_s[k] = s
+                    out_row[k] = soff[s, d, e] + (row - lo)
+                    found = True
+                    break
+            if found:
+                break
+        if not found:
+            raise IndexError("row beyond the receive buffer")
+    return out_s, out_row
