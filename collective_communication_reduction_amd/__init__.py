@@ -1,0 +1,288 @@
+"""Gradient-synchronisation collectives on one MI355X: Python binding of libgc.
+
+A thin ctypes layer over the C ABI declared in include/gc.h.  It only marshals
+arguments: it turns lists of tensors (or raw device addresses) into pointer
+arrays, maps dtype/op/order names onto the C enums, passes torch's current HIP
+stream, and raises GcError for a non-OK status.  Every collective runs in the
+HIP kernels of libgc.so; there is no other implementation to fall back to, and
+importing this package fails if the library has not been built
+(python collective_communication_reduction_amd/build.py).
+
+The functions carry the C names:
+  gc_all_reduce, gc_reduce_scatter, gc_all_gather, gc_all_to_all,
+  gc_all_reduce_scratch_bytes, gc_bucket_plan_create / _query / _destroy,
+  gc_bucket_pack, gc_bucket_unpack, gc_status_string, gc_version
+plus BucketPlan, a small owner of a gc_bucket_plan handle.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python collective_communication_reduction_amd/build.py)")
+
+# PyTorch ships its own HIP runtime, which its libraries request as
+# "libamdhip64.so"; libgc requests "libamdhip64.so.7".  Importing torch first
+# makes libgc bind to the runtime already in the process, so both sides share
+# one runtime (and torch's streams and allocations are valid for libgc).
+# Loading libgc first would pull in the system runtime as a second copy.
+try:
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - the library itself does not need torch
+    torch = None
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+GC_MAX_RANKS = 64
+GC_OK, GC_ERR_INVALID_ARG, GC_ERR_UNSUPPORTED, GC_ERR_HIP, GC_ERR_NO_MEMORY = range(5)
+GC_INT32, GC_FP32, GC_BF16 = 0, 1, 2
+GC_SUM, GC_AVG = 0, 1
+GC_ORDER_RING, GC_ORDER_RANK = 0, 1
+GC_AR_FUSED, GC_AR_RS_AG = 0, 1
+SIZE_MAX = (1 << 64) - 1
+
+_DTYPE = {"int32": GC_INT32, "fp32": GC_FP32, "bf16": GC_BF16}
+_OP = {"sum": GC_SUM, "avg": GC_AVG}
+_ORDER = {"ring": GC_ORDER_RING, "rank": GC_ORDER_RANK}
+_ALGO = {"fused": GC_AR_FUSED, "rs_ag": GC_AR_RS_AG}
+
+_vp, _sz, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_VPP = ctypes.POINTER(ctypes.c_void_p)
+
+
+def _sig(name, restype, *argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+    return f
+
+
+_c_rs = _sig("gc_reduce_scatter", _int, _VPP, _VPP, _sz, _int, _int, _int, _int, _int, _vp)
+_c_ag = _sig("gc_all_gather", _int, _VPP, _VPP, _sz, _int, _int, _vp)
+_c_ar_scratch = _sig("gc_all_reduce_scratch_bytes", _sz, _sz, _int, _int, _int)
+_c_ar = _sig("gc_all_reduce", _int, _VPP, _VPP, _sz, _int, _int, _int, _int, _int, _vp, _sz, _vp)
+_c_a2a = _sig("gc_all_to_all", _int, _VPP, _VPP, ctypes.POINTER(ctypes.c_int64), _int, _int, _sz, _vp)
+_c_plan_create = _sig("gc_bucket_plan_create", _int, ctypes.POINTER(ctypes.c_size_t), _int, _int, _sz, _int, _sz,
+                      ctypes.POINTER(_vp))
+_c_plan_query = _sig("gc_bucket_plan_query", _int, _vp, ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_size_t),
+                     ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_size_t))
+_c_pack = _sig("gc_bucket_pack", _int, _vp, _int, _VPP, _VPP, _int, _vp)
+_c_unpack = _sig("gc_bucket_unpack", _int, _vp, _int, _VPP, _VPP, _int, _vp)
+_c_plan_destroy = _sig("gc_bucket_plan_destroy", None, _vp)
+_c_status = _sig("gc_status_string", ctypes.c_char_p, _int)
+_c_version = _sig("gc_version", _int)
+_c_last_hip = _sig("gc_last_hip_error", _int)
+
+
+class GcError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        detail = f" (hipError_t {gc_last_hip_error()})" if status == GC_ERR_HIP else ""
+        super().__init__(f"{what}: {gc_status_string(status)}{detail}")
+
+
+def gc_last_hip_error():
+    """hipError_t of the last HIP call that failed inside libgc on this thread (0 if none)."""
+    return _c_last_hip()
+
+
+def gc_status_string(status):
+    return _c_status(int(status)).decode()
+
+
+def gc_version():
+    return _c_version()
+
+
+def _check(status, what):
+    if status != GC_OK:
+        raise GcError(status, what)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _addr(x):
+    """Device address of a tensor (data_ptr) or a raw integer address; None -> NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _ptr_array(xs):
+    if xs is None:
+        return None
+    arr = (ctypes.c_void_p * max(1, len(xs)))()
+    for i, x in enumerate(xs):
+        arr[i] = _addr(x)
+    return arr
+
+
+def _dtype_code(x):
+    if isinstance(x, str):
+        return _DTYPE[x]
+    if isinstance(x, int):
+        return x
+    import torch
+    return {torch.bfloat16: GC_BF16, torch.float32: GC_FP32, torch.int32: GC_INT32}[x]
+
+
+def _enum(table, x):
+    return table[x] if isinstance(x, str) else int(x)
+
+
+def _stream(stream, like=None):
+    """HIP stream handle: an explicit int / torch stream, else torch's current stream on like's device."""
+    if stream is None:
+        import torch
+        dev = like.device if hasattr(like, "device") and like.device.type == "cuda" else None
+        if dev is None and not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _first(xs):
+    return xs[0] if xs else None
+
+
+def _numel(xs, count):
+    if count is not None:
+        return int(count)
+    return int(xs[0].numel())
+
+
+def _infer_dtype(xs, dtype):
+    if dtype is not None:
+        return _dtype_code(dtype)
+    return _dtype_code(xs[0].dtype)
+
+
+# ------------------------------------------------------------------ collectives
+
+def gc_all_reduce(send, recv=None, op="avg", order="ring", algo="fused", scratch=None, scratch_bytes=None,
+                  count=None, dtype=None, stream=None):
+    """All-reduce N rank buffers; recv defaults to send (in place).  See include/gc.h."""
+    recv = send if recv is None else recv
+    n = len(send)
+    t = _infer_dtype(send, dtype)
+    cnt = _numel(send, count)
+    a = _enum(_ALGO, algo)
+    if scratch_bytes is None:
+        scratch_bytes = scratch.numel() * scratch.element_size() if hasattr(scratch, "numel") else 0
+    _check(_c_ar(_ptr_array(send), _ptr_array(recv), cnt, n, t, _enum(_OP, op), _enum(_ORDER, order), a,
+                 _addr(scratch), int(scratch_bytes), _stream(stream, _first(send))), "gc_all_reduce")
+    return recv
+
+
+def gc_all_reduce_scratch_bytes(count, nranks, dtype, algo="rs_ag"):
+    return int(_c_ar_scratch(int(count), int(nranks), _dtype_code(dtype), _enum(_ALGO, algo)))
+
+
+def gc_reduce_scatter(send, recv, op="avg", order="ring", recv_count=None, in_dtype=None, out_dtype=None,
+                      stream=None):
+    """Reduce-scatter: recv[j] = op_i send[i][j*recv_count : (j+1)*recv_count]."""
+    n = len(send)
+    ti = _infer_dtype(send, in_dtype)
+    to = _infer_dtype(recv, out_dtype)
+    rc = _numel(recv, recv_count)
+    _check(_c_rs(_ptr_array(send), _ptr_array(recv), rc, n, ti, to, _enum(_OP, op), _enum(_ORDER, order),
+                 _stream(stream, _first(send))), "gc_reduce_scatter")
+    return recv
+
+
+def gc_all_gather(send, recv, count=None, dtype=None, stream=None):
+    """All-gather: recv[d][i*count : (i+1)*count] = send[i] for every d."""
+    n = len(send)
+    t = _infer_dtype(send, dtype)
+    cnt = _numel(send, count)
+    _check(_c_ag(_ptr_array(send), _ptr_array(recv), cnt, n, t, _stream(stream, _first(send))), "gc_all_gather")
+    return recv
+
+
+def gc_all_to_all(send, recv, splits, row_bytes, stream=None):
+    """All-to-all(v) with experts: splits is an int64 array-like [N][N][E] of rows."""
+    import numpy as np
+    sp = np.ascontiguousarray(np.asarray(splits, dtype=np.int64))
+    if sp.ndim != 3:
+        raise ValueError("splits must be [N][N][E]")
+    n, _, e = sp.shape
+    _check(_c_a2a(_ptr_array(send), _ptr_array(recv), sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, e,
+                  int(row_bytes), _stream(stream, _first(send))), "gc_all_to_all")
+    return recv
+
+
+# ------------------------------------------------------------------ bucket plan
+
+def gc_bucket_plan_create(numels, dtype, cap_bytes, reverse=True, pad_to=1):
+    arr = (ctypes.c_size_t * max(1, len(numels)))(*[int(x) for x in numels])
+    out = ctypes.c_void_p()
+    _check(_c_plan_create(arr, len(numels), _dtype_code(dtype), int(cap_bytes), int(bool(reverse)), int(pad_to),
+                          ctypes.byref(out)), "gc_bucket_plan_create")
+    return out.value
+
+
+def gc_bucket_plan_query(plan, ntensors):
+    nb = ctypes.c_int()
+    _check(_c_plan_query(plan, ctypes.byref(nb), None, None, None), "gc_bucket_plan_query")
+    bucket_numel = (ctypes.c_size_t * max(1, nb.value))()
+    tb = (ctypes.c_int * max(1, ntensors))()
+    to = (ctypes.c_size_t * max(1, ntensors))()
+    _check(_c_plan_query(plan, ctypes.byref(nb), bucket_numel, tb, to), "gc_bucket_plan_query")
+    return (nb.value, [bucket_numel[i] for i in range(nb.value)], [tb[i] for i in range(ntensors)],
+            [to[i] for i in range(ntensors)])
+
+
+def gc_bucket_plan_destroy(plan):
+    _c_plan_destroy(plan)
+
+
+def gc_bucket_pack(plan, bucket, tensors, bucket_bufs, nranks, stream=None):
+    """tensors: flat rank-major list of nranks*ntensors tensors (or None for tensors outside the bucket)."""
+    _check(_c_pack(plan, int(bucket), _ptr_array(tensors), _ptr_array(bucket_bufs), int(nranks),
+                   _stream(stream, _first(bucket_bufs))), "gc_bucket_pack")
+
+
+def gc_bucket_unpack(plan, bucket, bucket_bufs, tensors, nranks, stream=None):
+    _check(_c_unpack(plan, int(bucket), _ptr_array(bucket_bufs), _ptr_array(tensors), int(nranks),
+                     _stream(stream, _first(bucket_bufs))), "gc_bucket_unpack")
+
+
+class BucketPlan:
+    """Owns a gc_bucket_plan handle and caches its query results."""
+
+    def __init__(self, numels, dtype, cap_bytes, reverse=True, pad_to=1):
+        self.numels = [int(x) for x in numels]
+        self.handle = gc_bucket_plan_create(self.numels, dtype, cap_bytes, reverse, pad_to)
+        self.nbuckets, self.bucket_numel, self.tensor_bucket, self.tensor_offset = gc_bucket_plan_query(
+            self.handle, len(self.numels))
+
+    def bucket_tensors(self, b):
+        """Tensor indices of bucket b in packing order."""
+        ts = [t for t in range(len(self.numels)) if self.tensor_bucket[t] == b]
+        return sorted(ts, key=lambda t: self.tensor_offset[t])
+
+    def pack(self, bucket, tensors, bucket_bufs, nranks, stream=None):
+        gc_bucket_pack(self.handle, bucket, tensors, bucket_bufs, nranks, stream)
+
+    def unpack(self, bucket, bucket_bufs, tensors, nranks, stream=None):
+        gc_bucket_unpack(self.handle, bucket, bucket_bufs, tensors, nranks, stream)
+
+    def close(self):
+        if self.handle:
+            gc_bucket_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,410 @@
+// C ABI of libgc: argument validation, aliasing rules, chunk / bucket /
+// all-to-all planning on the host, then the kernel launches.  Every check runs
+// before anything is enqueued, so a non-OK status means no work was launched.
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "gc.h"
+#include "gc_internal.h"
+
+namespace {
+
+using gci::elem_bytes;
+
+bool valid_dtype(gc_dtype t) { return t == GC_INT32 || t == GC_FP32 || t == GC_BF16; }
+bool valid_op(gc_op op) { return op == GC_SUM || op == GC_AVG; }
+bool valid_order(gc_order o) { return o == GC_ORDER_RING || o == GC_ORDER_RANK; }
+
+uint64_t addr(const void* p) { return reinterpret_cast<uint64_t>(p); }
+
+// Byte interval [lo, hi) of a buffer.
+struct Span {
+  uint64_t lo, hi;
+  bool empty() const { return hi <= lo; }
+};
+
+Span span(const void* p, uint64_t bytes) { return Span{addr(p), addr(p) + bytes}; }
+
+bool overlaps(const Span& a, const Span& b) { return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi; }
+
+// True if any two spans of `w` overlap.
+bool any_overlap(std::vector<Span> w) {
+  std::sort(w.begin(), w.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  uint64_t reach = 0;
+  bool first = true;
+  for (const Span& s : w) {
+    if (s.empty()) continue;
+    if (!first && s.lo < reach) return true;
+    reach = first ? s.hi : std::max(reach, s.hi);
+    first = false;
+  }
+  return false;
+}
+
+bool mul_overflows(uint64_t a, uint64_t b) { return b != 0 && a > UINT64_MAX / b; }
+
+gc_status check_ranks(int nranks) {
+  if (nranks < 1) return GC_ERR_INVALID_ARG;
+  if (nranks > GC_MAX_RANKS) return GC_ERR_UNSUPPORTED;
+  return GC_OK;
+}
+
+gc_status check_ptrs(const void* const* p, int n, size_t es) {
+  if (!p) return GC_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (!p[i] || addr(p[i]) % es) return GC_ERR_INVALID_ARG;
+  return GC_OK;
+}
+
+#define GC_TRY(expr)                    \
+  do {                                  \
+    const gc_status _s = (expr);        \
+    if (_s != GC_OK) return _s;         \
+  } while (0)
+
+}  // namespace
+
+// --------------------------------------------------------------------- status
+
+extern "C" const char* gc_status_string(gc_status s) {
+  switch (s) {
+    case GC_OK: return "GC_OK";
+    case GC_ERR_INVALID_ARG: return "GC_ERR_INVALID_ARG";
+    case GC_ERR_UNSUPPORTED: return "GC_ERR_UNSUPPORTED";
+    case GC_ERR_HIP: return "GC_ERR_HIP";
+    case GC_ERR_NO_MEMORY: return "GC_ERR_NO_MEMORY";
+  }
+  return "GC_ERR_UNKNOWN";
+}
+
+extern "C" int gc_version(void) { return 100; }
+
+namespace {
+thread_local int g_last_hip_error = 0;
+}  // namespace
+
+gc_status gci::hip_status(hipError_t e) {
+  if (e == hipSuccess) return GC_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return GC_ERR_HIP;
+}
+
+extern "C" int gc_last_hip_error(void) { return g_last_hip_error; }
+
+// ------------------------------------------------------------- reduce-scatter
+
+extern "C" gc_status gc_reduce_scatter(const void* const* send, void* const* recv, size_t recv_count,
+                                       int nranks, gc_dtype in_t, gc_dtype out_t, gc_op op,
+                                       gc_order order, hipStream_t stream) {
+  GC_TRY(check_ranks(nranks));
+  if (!valid_dtype(in_t) || !valid_dtype(out_t) || !valid_op(op) || !valid_order(order) || !send || !recv)
+    return GC_ERR_INVALID_ARG;
+  if ((in_t == GC_INT32) != (out_t == GC_INT32)) return GC_ERR_UNSUPPORTED;
+  if (op == GC_AVG && in_t == GC_INT32) return GC_ERR_UNSUPPORTED;
+  const uint64_t N = static_cast<uint64_t>(nranks);
+  if (mul_overflows(recv_count, N) || mul_overflows(recv_count * N, 4)) return GC_ERR_INVALID_ARG;
+  if (recv_count == 0) return GC_OK;
+  const size_t ei = elem_bytes(in_t), eo = elem_bytes(out_t);
+  GC_TRY(check_ptrs(send, nranks, ei));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, eo));
+
+  // Aliasing: recv[r] may sit exactly on chunk r of send[r] when types match;
+  // recv spans must not overlap each other nor any other part of any send.
+  std::vector<Span> outs;
+  for (int r = 0; r < nranks; ++r) outs.push_back(span(recv[r], recv_count * eo));
+  if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
+  for (int r = 0; r < nranks; ++r) {
+    const bool in_place = in_t == out_t && addr(recv[r]) == addr(send[r]) + r * recv_count * ei;
+    for (int i = 0; i < nranks; ++i) {
+      const Span in = span(send[i], N * recv_count * ei);
+      if (!overlaps(outs[r], in)) continue;
+      if (in_place && i == r) continue;
+      return GC_ERR_INVALID_ARG;
+    }
+  }
+  gci::ReduceCall c{send, recv, nranks, N * recv_count, recv_count, in_t, out_t,
+                    op == GC_AVG, order == GC_ORDER_RING, stream};
+  return gci::launch_reduce_scatter(c);
+}
+
+// ----------------------------------------------------------------- all-gather
+
+extern "C" gc_status gc_all_gather(const void* const* send, void* const* recv, size_t count, int nranks,
+                                   gc_dtype t, hipStream_t stream) {
+  GC_TRY(check_ranks(nranks));
+  if (!valid_dtype(t) || !send || !recv) return GC_ERR_INVALID_ARG;
+  const uint64_t N = static_cast<uint64_t>(nranks);
+  if (mul_overflows(count, N) || mul_overflows(count * N, 4)) return GC_ERR_INVALID_ARG;
+  if (count == 0) return GC_OK;
+  const size_t es = elem_bytes(t);
+  GC_TRY(check_ptrs(send, nranks, es));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es));
+
+  // Aliasing: send[r] may sit exactly on slot r of recv[r]; otherwise no overlap.
+  std::vector<Span> outs;
+  for (int r = 0; r < nranks; ++r) outs.push_back(span(recv[r], N * count * es));
+  if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
+  for (int i = 0; i < nranks; ++i) {
+    const Span in = span(send[i], count * es);
+    const bool in_place = addr(send[i]) == addr(recv[i]) + i * count * es;
+    for (int r = 0; r < nranks; ++r) {
+      if (!overlaps(outs[r], in)) continue;
+      if (in_place && r == i) continue;
+      return GC_ERR_INVALID_ARG;
+    }
+  }
+  gci::ReduceCall c{send, recv, nranks, N * count, count, t, t, false, false, stream};
+  return gci::launch_all_gather(c);
+}
+
+// ----------------------------------------------------------------- all-reduce
+
+namespace {
+
+uint64_t chunk_len(uint64_t count, int nranks) { return (count + nranks - 1) / nranks; }
+
+}  // namespace
+
+extern "C" size_t gc_all_reduce_scratch_bytes(size_t count, int nranks, gc_dtype t, gc_ar_algo algo) {
+  if (algo != GC_AR_RS_AG || !valid_dtype(t) || nranks < 1) return 0;
+  if (mul_overflows(count, 4)) return 0;
+  return (count * elem_bytes(t) + 255) / 256 * 256;
+}
+
+extern "C" gc_status gc_all_reduce(const void* const* send, void* const* recv, size_t count, int nranks,
+                                   gc_dtype t, gc_op op, gc_order order, gc_ar_algo algo, void* scratch,
+                                   size_t scratch_bytes, hipStream_t stream) {
+  GC_TRY(check_ranks(nranks));
+  if (!valid_dtype(t) || !valid_op(op) || !valid_order(order) || !send || !recv) return GC_ERR_INVALID_ARG;
+  if (algo != GC_AR_FUSED && algo != GC_AR_RS_AG) return GC_ERR_INVALID_ARG;
+  if (op == GC_AVG && t == GC_INT32) return GC_ERR_UNSUPPORTED;
+  if (mul_overflows(count, 4)) return GC_ERR_INVALID_ARG;
+  if (count == 0) return GC_OK;
+  const size_t es = elem_bytes(t);
+  GC_TRY(check_ptrs(send, nranks, es));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es));
+
+  // Aliasing: each recv[r] is disjoint from every send[i] or equal to it.
+  const uint64_t bytes = count * es;
+  std::vector<Span> outs;
+  for (int r = 0; r < nranks; ++r) outs.push_back(span(recv[r], bytes));
+  if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
+  for (int r = 0; r < nranks; ++r)
+    for (int i = 0; i < nranks; ++i)
+      if (overlaps(outs[r], span(send[i], bytes)) && addr(recv[r]) != addr(send[i])) return GC_ERR_INVALID_ARG;
+
+  const uint64_t c = chunk_len(count, nranks);
+  if (algo == GC_AR_FUSED) {
+    gci::ReduceCall call{send, recv, nranks, count, c, t, t, op == GC_AVG, order == GC_ORDER_RING, stream};
+    return gci::launch_all_reduce(call);
+  }
+
+  if (!scratch || addr(scratch) % es || scratch_bytes < gc_all_reduce_scratch_bytes(count, nranks, t, algo))
+    return GC_ERR_INVALID_ARG;
+  const Span sc = span(scratch, bytes);
+  for (int r = 0; r < nranks; ++r)
+    if (overlaps(sc, outs[r]) || overlaps(sc, span(send[r], bytes))) return GC_ERR_INVALID_ARG;
+
+  // Owner chunk j lives at scratch + j*c elements: reduce-scatter writes it
+  // (averaged and rounded), all-gather reads it back out to every rank.
+  std::vector<void*> shard_out(nranks);
+  std::vector<const void*> shard_in(nranks);
+  for (int j = 0; j < nranks; ++j) {
+    const uint64_t lo = std::min<uint64_t>(count, static_cast<uint64_t>(j) * c);
+    shard_out[j] = static_cast<char*>(scratch) + lo * es;
+    shard_in[j] = shard_out[j];
+  }
+  gci::ReduceCall rs{send, shard_out.data(), nranks, count, c, t, t, op == GC_AVG, order == GC_ORDER_RING, stream};
+  GC_TRY(gci::launch_reduce_scatter(rs));
+  gci::ReduceCall ag{shard_in.data(), recv, nranks, count, c, t, t, false, false, stream};
+  return gci::launch_all_gather(ag);
+}
+
+// ----------------------------------------------------------------- all-to-all
+
+extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, const int64_t* splits,
+                                   int nranks, int experts_per_rank, size_t row_bytes, hipStream_t stream) {
+  GC_TRY(check_ranks(nranks));
+  if (!send || !recv || !splits || experts_per_rank < 1 || row_bytes == 0) return GC_ERR_INVALID_ARG;
+  const int N = nranks, E = experts_per_rank;
+  if (static_cast<int64_t>(N) * E > gci::kA2AMaxBlocks) return GC_ERR_UNSUPPORTED;
+
+  std::vector<int64_t> send_rows(N, 0), recv_rows(N, 0);
+  for (int s = 0; s < N; ++s)
+    for (int d = 0; d < N; ++d)
+      for (int e = 0; e < E; ++e) {
+        const int64_t v = splits[(static_cast<int64_t>(s) * N + d) * E + e];
+        if (v < 0) return GC_ERR_INVALID_ARG;
+        send_rows[s] += v;
+        recv_rows[d] += v;
+        if (send_rows[s] >= (int64_t(1) << 31) || recv_rows[d] >= (int64_t(1) << 31)) return GC_ERR_UNSUPPORTED;
+      }
+  int64_t total = 0;
+  for (int s = 0; s < N; ++s) total += send_rows[s];
+  if (total >= (int64_t(1) << 31)) return GC_ERR_UNSUPPORTED;
+  for (int s = 0; s < N; ++s)
+    if (mul_overflows(static_cast<uint64_t>(send_rows[s]), row_bytes) ||
+        mul_overflows(static_cast<uint64_t>(recv_rows[s]), row_bytes))
+      return GC_ERR_INVALID_ARG;
+  if (total == 0) return GC_OK;
+
+  std::vector<Span> all;
+  for (int r = 0; r < N; ++r) {
+    if ((send_rows[r] && !send[r]) || (recv_rows[r] && !recv[r])) return GC_ERR_INVALID_ARG;
+    all.push_back(span(recv[r], recv_rows[r] * row_bytes));
+  }
+  if (any_overlap(all)) return GC_ERR_INVALID_ARG;
+  for (int r = 0; r < N; ++r)
+    for (int s = 0; s < N; ++s)
+      if (overlaps(all[r], span(send[s], send_rows[s] * row_bytes))) return GC_ERR_INVALID_ARG;
+
+  // Destinations are split into groups small enough for one launch each.
+  const int dg = std::max(1, gci::kA2AMaxBlocks / (N * E));
+  std::vector<int32_t> base(N, 0), rows;
+  for (int d0 = 0; d0 < N; d0 += dg) {
+    const int dc = std::min(dg, N - d0);
+    rows.assign(static_cast<size_t>(N) * dc * E, 0);
+    for (int s = 0; s < N; ++s)
+      for (int dl = 0; dl < dc; ++dl)
+        for (int e = 0; e < E; ++e)
+          rows[(static_cast<size_t>(s) * dc + dl) * E + e] =
+              static_cast<int32_t>(splits[(static_cast<int64_t>(s) * N + d0 + dl) * E + e]);
+    gci::A2ACall call{send, recv, N, E, d0, dc, row_bytes, base.data(), rows.data(), stream};
+    GC_TRY(gci::launch_all_to_all(call));
+    for (int s = 0; s < N; ++s)
+      for (int dl = 0; dl < dc; ++dl)
+        for (int e = 0; e < E; ++e) base[s] += rows[(static_cast<size_t>(s) * dc + dl) * E + e];
+  }
+  return GC_OK;
+}
+
+// ---------------------------------------------------------------- bucket plan
+
+struct gc_bucket_plan {
+  gc_dtype t;
+  size_t es;
+  std::vector<size_t> numel;
+  std::vector<int> tensor_bucket;
+  std::vector<size_t> tensor_offset;
+  std::vector<std::vector<int>> buckets;  // tensor indices in packing order
+  std::vector<size_t> used;               // elements of real data per bucket
+  std::vector<size_t> padded;             // elements after zero padding
+};
+
+extern "C" gc_status gc_bucket_plan_create(const size_t* numels, int ntensors, gc_dtype t, size_t cap_bytes,
+                                           int reverse, size_t pad_to, gc_bucket_plan** out) {
+  if (!out) return GC_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (ntensors < 0 || (ntensors > 0 && !numels) || !valid_dtype(t) || pad_to == 0) return GC_ERR_INVALID_ARG;
+  gc_bucket_plan* p = new (std::nothrow) gc_bucket_plan;
+  if (!p) return GC_ERR_NO_MEMORY;
+  try {
+    p->t = t;
+    p->es = elem_bytes(t);
+    p->numel.assign(numels, numels + ntensors);
+    p->tensor_bucket.assign(ntensors, -1);
+    p->tensor_offset.assign(ntensors, 0);
+    std::vector<int> cur;
+    size_t cur_elems = 0;
+    auto close = [&]() {
+      size_t run = 0;
+      for (int ti : cur) {
+        p->tensor_bucket[ti] = static_cast<int>(p->buckets.size());
+        p->tensor_offset[ti] = run;
+        run += p->numel[ti];
+      }
+      p->buckets.push_back(cur);
+      p->used.push_back(run);
+      p->padded.push_back((run + pad_to - 1) / pad_to * pad_to);
+      cur.clear();
+      cur_elems = 0;
+    };
+    for (int k = 0; k < ntensors; ++k) {
+      const int ti = reverse ? ntensors - 1 - k : k;
+      if (mul_overflows(p->numel[ti], 4) || cur_elems + p->numel[ti] < cur_elems) {
+        delete p;
+        return GC_ERR_INVALID_ARG;
+      }
+      cur.push_back(ti);
+      cur_elems += p->numel[ti];
+      if (cap_bytes != SIZE_MAX && cur_elems * p->es >= cap_bytes) close();
+    }
+    if (!cur.empty()) close();
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return GC_ERR_NO_MEMORY;
+  }
+  *out = p;
+  return GC_OK;
+}
+
+extern "C" gc_status gc_bucket_plan_query(const gc_bucket_plan* p, int* nbuckets, size_t* bucket_numel,
+                                          int* tensor_bucket, size_t* tensor_offset) {
+  if (!p) return GC_ERR_INVALID_ARG;
+  if (nbuckets) *nbuckets = static_cast<int>(p->buckets.size());
+  if (bucket_numel) std::copy(p->padded.begin(), p->padded.end(), bucket_numel);
+  if (tensor_bucket) std::copy(p->tensor_bucket.begin(), p->tensor_bucket.end(), tensor_bucket);
+  if (tensor_offset) std::copy(p->tensor_offset.begin(), p->tensor_offset.end(), tensor_offset);
+  return GC_OK;
+}
+
+extern "C" void gc_bucket_plan_destroy(gc_bucket_plan* p) { delete p; }
+
+namespace {
+
+// Segments of one bucket for every rank; pack copies tensor -> bucket (plus
+// zero padding), unpack copies bucket -> tensor.
+gc_status bucket_segments(const gc_bucket_plan* p, int bucket, const void* const* tensors,
+                          void* const* tensor_out, const void* const* bufs_in, void* const* bufs_out,
+                          int nranks, bool packing, std::vector<gci::Segment>* segs) {
+  GC_TRY(check_ranks(nranks));
+  if (!p || bucket < 0 || bucket >= static_cast<int>(p->buckets.size())) return GC_ERR_INVALID_ARG;
+  const size_t T = p->numel.size();
+  const std::vector<int>& b = p->buckets[bucket];
+  const size_t es = p->es;
+  std::vector<Span> writes, reads;
+  for (int r = 0; r < nranks; ++r) {
+    const void* buf_r = packing ? static_cast<const void*>(bufs_out[r]) : bufs_in[r];
+    if (p->padded[bucket] && (!buf_r || addr(buf_r) % es)) return GC_ERR_INVALID_ARG;
+    const Span bspan = span(buf_r, p->padded[bucket] * es);
+    (packing ? writes : reads).push_back(bspan);
+    for (int ti : b) {
+      const size_t n = p->numel[ti];
+      if (!n) continue;
+      const void* tp = packing ? tensors[r * T + ti] : static_cast<const void*>(tensor_out[r * T + ti]);
+      if (!tp || addr(tp) % es) return GC_ERR_INVALID_ARG;
+      (packing ? reads : writes).push_back(span(tp, n * es));
+      char* bb = static_cast<char*>(const_cast<void*>(buf_r)) + p->tensor_offset[ti] * es;
+      if (packing) segs->push_back(gci::Segment{tp, bb, n * es});
+      else segs->push_back(gci::Segment{bb, const_cast<void*>(tp), n * es});
+    }
+    if (packing && p->padded[bucket] > p->used[bucket])
+      segs->push_back(gci::Segment{nullptr, static_cast<char*>(bufs_out[r]) + p->used[bucket] * es,
+                                   (p->padded[bucket] - p->used[bucket]) * es});
+  }
+  if (any_overlap(writes)) return GC_ERR_INVALID_ARG;
+  for (const Span& w : writes)
+    for (const Span& rd : reads)
+      if (overlaps(w, rd)) return GC_ERR_INVALID_ARG;
+  return GC_OK;
+}
+
+}  // namespace
+
+extern "C" gc_status gc_bucket_pack(const gc_bucket_plan* p, int bucket, const void* const* tensors,
+                                    void* const* bucket_bufs, int nranks, hipStream_t stream) {
+  if (!tensors || !bucket_bufs) return GC_ERR_INVALID_ARG;
+  std::vector<gci::Segment> segs;
+  GC_TRY(bucket_segments(p, bucket, tensors, nullptr, nullptr, bucket_bufs, nranks, true, &segs));
+  return gci::launch_segment_copy(segs.data(), segs.size(), stream);
+}
+
+extern "C" gc_status gc_bucket_unpack(const gc_bucket_plan* p, int bucket, const void* const* bucket_bufs,
+                                      void* const* tensors, int nranks, hipStream_t stream) {
+  if (!tensors || !bucket_bufs) return GC_ERR_INVALID_ARG;
+  std::vector<gci::Segment> segs;
+  GC_TRY(bucket_segments(p, bucket, nullptr, tensors, bucket_bufs, nullptr, nranks, false, &segs));
+  return gci::launch_segment_copy(segs.data(), segs.size(), stream);
+}

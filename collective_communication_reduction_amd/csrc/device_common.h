@@ -1,0 +1,89 @@
+// Device-side helpers for the gfx950 kernels: 16-byte non-temporal vector
+// access, element unpack/pack for the three supported types, and the
+// averaging epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gcdev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;  // four 64-wide wavefronts per workgroup
+
+// Streaming data is touched exactly once per launch, so loads and stores carry
+// the non-temporal hint: they should not displace other data in L2 / MALL.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st8(void* p, u32x2 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+
+// ---------------------------------------------------------------- inputs
+// In::VE elements fill one 16-byte vector; In::Acc is the reduction type
+// (fp32 for bf16 / fp32 data, uint32 with wrap-around for int32 data).
+
+struct InBf16 {
+  static constexpr int VE = 8;
+  static constexpr int ES = 2;
+  typedef float Acc;
+  __device__ static __forceinline__ float one(const void* base, uint64_t e) {
+    const uint16_t b = reinterpret_cast<const uint16_t*>(base)[e];
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+  }
+};
+
+struct InF32 {
+  static constexpr int VE = 4;
+  static constexpr int ES = 4;
+  typedef float Acc;
+  __device__ static __forceinline__ float one(const void* base, uint64_t e) {
+    return reinterpret_cast<const float*>(base)[e];
+  }
+};
+
+struct InI32 {
+  static constexpr int VE = 4;
+  static constexpr int ES = 4;
+  typedef uint32_t Acc;
+  __device__ static __forceinline__ uint32_t one(const void* base, uint64_t e) {
+    return reinterpret_cast<const uint32_t*>(base)[e];
+  }
+};
+
+// ---------------------------------------------------------------- epilogue
+// Average: one correctly rounded fp32 division by N.  Integers never average.
+__device__ __forceinline__ float finish(float x, bool avg, float n) { return avg ? __fdiv_rn(x, n) : x; }
+__device__ __forceinline__ uint32_t finish(uint32_t x, bool, float) { return x; }
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)));
+}
+
+// ---------------------------------------------------------------- outputs
+// Element size of each output type, and the bytes one vector of VE results
+// occupies (the store width the output alignment is checked against).
+
+struct OutBf16 {
+  static constexpr int ES = 2;
+  static constexpr int vec_bytes(int VE) { return 2 * VE; }
+};
+
+struct OutF32 {
+  static constexpr int ES = 4;
+  static constexpr int vec_bytes(int VE) { return 4 * VE; }
+};
+
+struct OutI32 {
+  static constexpr int ES = 4;
+  static constexpr int vec_bytes(int VE) { return 4 * VE; }
+};
+
+}  // namespace gcdev

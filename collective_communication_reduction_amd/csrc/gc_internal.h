@@ -1,0 +1,71 @@
+// Internal interface between the C ABI layer (api.cpp: validation, planning)
+// and the kernel launchers (reduce.hip, movement.hip).  Not installed.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gc.h"
+
+namespace gci {
+
+inline size_t elem_bytes(gc_dtype t) { return t == GC_BF16 ? 2 : 4; }
+
+// Maps a HIP result to a status, remembering a failure for gc_last_hip_error().
+gc_status hip_status(hipError_t e);
+
+// Geometry shared by the three reduction-family launches.  The reference index
+// space has S elements cut into N chunks [j*c, min(S, (j+1)*c)).
+//
+//   all_reduce:      in[i]  = rank i's buffer        (element E at in[i] + E)
+//                    out[r] = rank r's buffer        (element E at out[r] + E)
+//   reduce_scatter:  in[i]  = rank i's full buffer   (element E at in[i] + E)
+//                    out[j] = chunk j's destination  (element E at out[j] + E - j*c)
+//   all_gather:      in[i]  = shard i                (element E at in[i] + E - i*c)
+//                    out[d] = rank d's full buffer   (element E at out[d] + E)
+struct ReduceCall {
+  const void* const* in;
+  void* const* out;
+  int nranks;
+  uint64_t S;
+  uint64_t c;
+  gc_dtype in_t;
+  gc_dtype out_t;
+  bool avg;
+  bool ring;
+  hipStream_t stream;
+};
+
+gc_status launch_all_reduce(const ReduceCall& call);
+gc_status launch_reduce_scatter(const ReduceCall& call);
+gc_status launch_all_gather(const ReduceCall& call);
+
+// One contiguous copy; src == nullptr writes zeros.
+struct Segment {
+  const void* src;
+  void* dst;
+  uint64_t bytes;
+};
+
+gc_status launch_segment_copy(const Segment* segs, size_t nseg, hipStream_t stream);
+
+// One all-to-all launch covering destinations [d0, d0 + dcount).
+struct A2ACall {
+  const void* const* send;
+  void* const* recv;
+  int nranks;
+  int experts;
+  int d0;
+  int dcount;
+  uint64_t row_bytes;
+  const int32_t* send_base;  // [nranks] row offset in send[s] where destination d0 starts
+  const int32_t* rows;       // [nranks][dcount][experts] rows of each block
+  hipStream_t stream;
+};
+
+// Largest nranks * dcount * experts one launch can describe.
+constexpr int kA2AMaxBlocks = 512;
+
+gc_status launch_all_to_all(const A2ACall& call);
+
+}  // namespace gci

@@ -1,0 +1,194 @@
+/*
+ * gc.h — gradient-synchronisation collectives on one MI355X (gfx950).
+ *
+ * The N "ranks" of a data-parallel group are N buffers in one GPU's HBM; a
+ * collective is the reduction and data movement it performs on them, done by
+ * hand-written HIP kernels.  Semantics follow the pages cited per call:
+ *
+ *   DTLM  "Distributed Training for Large Models: Collectives, FSDP/ZeRO,
+ *         DeviceMesh, and Multi-Dimensional Parallelism" (zexinliu.github.io)
+ *   AIG6  "AI Infra Guide", chapter 6 "分布式训练基础" (theaiera.top)
+ *   NXMR  the nxmr.cn article on collective communication and model
+ *         parallelism (news/160867), by its own section numbers
+ *
+ * Conventions for every call
+ *   - Buffers are DEVICE pointers owned by the caller; arrays of pointers,
+ *     split tables and size lists are HOST arrays, read before the call returns.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without synchronising; results are visible to later work on that stream.
+ *   - Arguments are validated on the host first.  A status other than GC_OK
+ *     means nothing was enqueued.  GC_ERR_HIP means a launch failed; faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - No call allocates device memory.  The bucket plan is a host object.
+ *   - nranks is 1..GC_MAX_RANKS.  Element counts are per rank.
+ *   - Calls are reentrant; concurrent calls on different streams must not
+ *     write overlapping memory.
+ *
+ * Reduction arithmetic (AIG6 §6.3.4, reduce_dtype=float32): bf16 and fp32
+ * inputs are summed in fp32, int32 inputs with wrap-around.  GC_AVG divides
+ * the fp32 sum by nranks with one IEEE division, then the result is rounded to
+ * the output type (bf16: round to nearest, ties to even; NaN stays NaN;
+ * subnormals kept).
+ *
+ * Fold order.  GC_ORDER_RING folds chunk j (owned by rank j) starting from
+ * rank j+1's contribution and ending with rank j's, the order the ring
+ * reduce-scatter produces (DTLM §2 "Reduce-Scatter", N = 4 schedule; NXMR
+ * §2.2).  GC_ORDER_RANK folds ranks 0, 1, ..., N-1 for every element.  Each
+ * fold starts from its first operand, never from zero.
+ */
+#ifndef GC_H
+#define GC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GC_MAX_RANKS 64
+
+typedef enum {
+  GC_OK = 0,
+  GC_ERR_INVALID_ARG = 1,   /* null pointer, bad enum, size mismatch, illegal overlap        */
+  GC_ERR_UNSUPPORTED = 2,   /* valid request outside this library's limits (e.g. N > 64)     */
+  GC_ERR_HIP = 3,           /* a HIP runtime call failed (launch, device query)               */
+  GC_ERR_NO_MEMORY = 4      /* host allocation failed (bucket plan)                           */
+} gc_status;
+
+typedef enum { GC_INT32 = 0, GC_FP32 = 1, GC_BF16 = 2 } gc_dtype;
+typedef enum { GC_SUM = 0, GC_AVG = 1 } gc_op;                 /* GC_AVG: floating types only */
+typedef enum { GC_ORDER_RING = 0, GC_ORDER_RANK = 1 } gc_order;
+typedef enum { GC_AR_FUSED = 0, GC_AR_RS_AG = 1 } gc_ar_algo;
+
+/*
+ * Reduce-scatter (DTLM §2 "Reduce-Scatter"; FSDP gradient sync, DTLM §4 FSDP1).
+ *   send[i]  rank i's full buffer, nranks*recv_count elements of in_t
+ *            (chunk j = elements [j*recv_count, (j+1)*recv_count)).
+ *   recv[j]  owner j's shard, recv_count elements of out_t:
+ *            recv[j][k] = op over i of send[i][j*recv_count + k].
+ *   Types: bf16->bf16, bf16->fp32, fp32->fp32, fp32->bf16, int32->int32.
+ *   The caller pads so that nranks divides the full length, as FSDP pads its
+ *   FlatParameter (DTLM §4 FSDP1).
+ *   In place is allowed only as recv[r] == send[r] + r*recv_count elements with
+ *   in_t == out_t; any other overlap is rejected with GC_ERR_INVALID_ARG.
+ */
+gc_status gc_reduce_scatter(const void* const* send, void* const* recv, size_t recv_count,
+                            int nranks, gc_dtype in_t, gc_dtype out_t, gc_op op, gc_order order,
+                            hipStream_t stream);
+
+/*
+ * All-gather (DTLM §2 "All-Gather"; FSDP parameter unshard, DTLM §4 FSDP1).
+ *   send[i]  shard i, count elements of t.
+ *   recv[d]  nranks*count elements: recv[d][i*count + k] = send[i][k] for every d.
+ *   Pure data movement (bit-exact).  In place is allowed only as
+ *   send[r] == recv[r] + r*count elements.
+ */
+gc_status gc_all_gather(const void* const* send, void* const* recv, size_t count, int nranks,
+                        gc_dtype t, hipStream_t stream);
+
+/*
+ * Scratch bytes gc_all_reduce needs for `algo` (0 for GC_AR_FUSED; for
+ * GC_AR_RS_AG one owner-shard buffer of count elements, 256-byte aligned).
+ */
+size_t gc_all_reduce_scratch_bytes(size_t count, int nranks, gc_dtype t, gc_ar_algo algo);
+
+/*
+ * All-reduce (DTLM §2 "All-Reduce": All-Reduce = Reduce-Scatter + All-Gather;
+ * DDP gradient sync, AIG6 §6.2.4).
+ *   send[i], recv[i]  count elements of t each; any count (the ring's owner
+ *   chunks are c = ceil(count/nranks) elements, trailing chunks short or empty).
+ *   recv[r][e] = op over i of send[i][e] for every r, folded in `order`.
+ *   GC_AR_FUSED   one pass: every element's N inputs are read once and the
+ *                 result is written to all N outputs.
+ *   GC_AR_RS_AG   reduce-scatter into `scratch` (owner shards, already
+ *                 averaged and rounded), then all-gather from it; the result is
+ *                 bit-identical to GC_AR_FUSED.  scratch_bytes must be at least
+ *                 gc_all_reduce_scratch_bytes(); scratch may be NULL for FUSED.
+ *   In place (recv[r] == send[r]) is allowed; recv[r] may also equal any send[i]
+ *   exactly.  Partial overlaps, overlapping recv buffers, or scratch
+ *   overlapping a buffer are rejected.
+ */
+gc_status gc_all_reduce(const void* const* send, void* const* recv, size_t count, int nranks,
+                        gc_dtype t, gc_op op, gc_order order, gc_ar_algo algo,
+                        void* scratch, size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * All-to-all(v) with an expert dimension (DTLM §2 "All-to-All"; MoE dispatch
+ * and All-to-AllV, DTLM §8).
+ *   splits   HOST int64 array [nranks][nranks][experts_per_rank]: splits[s][d][e]
+ *            rows go from rank s to local expert e of rank d.
+ *   send[s]  rows grouped by destination d, then expert e (block (s,d,e) at row
+ *            offset sum of splits[s][d'][e'] over (d',e') before (d,e)).
+ *   recv[d]  rows grouped by expert e, then source s (block (s,d,e) at row
+ *            offset sum of splits[s'][d][e'] over (e',s') before (e,s)); rows of
+ *            a block keep their order.  With experts_per_rank == 1 this is
+ *            plain all_to_all_v ordered by source.
+ *   row_bytes bytes per row (any value >= 1).  Row counts per rank must be
+ *            below 2^31.  Pure data movement (bit-exact); buffers must not overlap.
+ */
+gc_status gc_all_to_all(const void* const* send, void* const* recv, const int64_t* splits,
+                        int nranks, int experts_per_rank, size_t row_bytes, hipStream_t stream);
+
+/*
+ * Bucket plan: DDP gradient buckets (AIG6 §6.2.4; NXMR §5.1) and the FSDP
+ * FlatParameter layout (DTLM §4 FSDP1).
+ *   Tensors are visited in reverse definition order when `reverse` is nonzero
+ *   (the order backward produces gradients), else in definition order.  Each
+ *   tensor is appended to the open bucket; the bucket closes as soon as its
+ *   bytes reach cap_bytes (cap_bytes == SIZE_MAX: one bucket holding all
+ *   tensors).  Tensors are never split.  Inside a bucket tensors are
+ *   concatenated in visiting order; each bucket's length is padded with zeros
+ *   to a multiple of pad_to elements (1: no padding; nranks: FlatParameter).
+ *   The plan is an immutable host object and may be shared across streams.
+ */
+typedef struct gc_bucket_plan gc_bucket_plan;
+
+gc_status gc_bucket_plan_create(const size_t* numels, int ntensors, gc_dtype t, size_t cap_bytes,
+                                int reverse, size_t pad_to, gc_bucket_plan** out);
+
+/*
+ * Query a plan.  Every output pointer may be NULL.
+ *   nbuckets        number of buckets.
+ *   bucket_numel    [nbuckets] padded element count of each bucket.
+ *   tensor_bucket   [ntensors] bucket index of each tensor.
+ *   tensor_offset   [ntensors] element offset of each tensor in its bucket.
+ */
+gc_status gc_bucket_plan_query(const gc_bucket_plan* plan, int* nbuckets, size_t* bucket_numel,
+                               int* tensor_bucket, size_t* tensor_offset);
+
+/*
+ * Pack bucket `bucket` of every rank: bucket_bufs[r][offset_t ...] = tensors[r*ntensors + t]
+ * for each tensor t of the bucket, and zeros in the padding.
+ *   tensors      HOST array of nranks*ntensors device pointers (rank-major); only
+ *                the bucket's tensors are read, others may be NULL.
+ *   bucket_bufs  nranks device buffers of at least bucket_numel elements.
+ * Pure data movement (bit-exact).  Buffers must not overlap.
+ */
+gc_status gc_bucket_pack(const gc_bucket_plan* plan, int bucket, const void* const* tensors,
+                         void* const* bucket_bufs, int nranks, hipStream_t stream);
+
+/* Inverse of gc_bucket_pack: tensors[r*ntensors + t] = bucket_bufs[r][offset_t ...]. */
+gc_status gc_bucket_unpack(const gc_bucket_plan* plan, int bucket, const void* const* bucket_bufs,
+                           void* const* tensors, int nranks, hipStream_t stream);
+
+void gc_bucket_plan_destroy(gc_bucket_plan* plan);
+
+/* Static, human-readable name of a status code. */
+const char* gc_status_string(gc_status status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int gc_version(void);
+
+/*
+ * hipError_t of the most recent HIP call that failed inside this library on
+ * the calling thread (the cause behind a GC_ERR_HIP), or 0 if none has failed.
+ */
+int gc_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GC_H */

@@ -1,0 +1,337 @@
+"""GPU parity: every libgc call against the CPU oracle, element by element, on
+seeded inputs at sizes that span several tiles and end in ragged tails, plus
+the degenerate cases (N = 1, empty, S < N, misaligned views, in place,
+special values).
+
+Tolerance: fp32 and int32 reductions and every data-movement call must be
+bit-exact; bf16 outputs must be within 1 bf16 ulp of the oracle's
+fp32-accumulated result (and are expected to be bit-exact, which is asserted
+separately)."""
+
+import numpy as np
+import pytest
+import torch
+
+import collective_communication_reduction_amd as gc
+from gen import host as G
+from oracle import buckets as OB
+from oracle import collectives as C
+from oracle.numerics import f32_to_bf16
+from tests.gpu_util import DEV, assert_same, empty, from_dev, max_ulp, to_dev
+
+pytestmark = pytest.mark.gpu
+
+ELEM = {"bf16": 2, "fp32": 4, "int32": 4}
+
+
+def _gen(dtype, N, S, seed, sigma=1e-3):
+    out = []
+    for r in range(N):
+        key = G.stream_key(seed, r, 0)
+        idx = np.arange(S)
+        if dtype == "bf16":
+            out.append(G.normal_bf16(key, idx, sigma))
+        elif dtype == "fp32":
+            out.append(G.uniform_f32(key, idx))
+        else:
+            out.append(G.int32_values(key, idx))
+    return out
+
+
+def _check(got, want, dtype, what):
+    if dtype == "bf16":
+        assert max_ulp(got, want) <= 1, what          # the contract: within 1 bf16 ulp
+    assert_same(got, want, dtype, what)               # expected: bit-exact
+
+
+# ------------------------------------------------------------------ all-reduce
+
+AR_SHAPES = [(1, 5), (2, 1), (3, 2), (4, 0), (4, 4096 * 3 + 13), (5, 12345), (7, 31), (8, 8 * 4096 * 2 + 5),
+             (8, 3), (16, 20000 + 7), (64, 64 * 600 + 9), (64, 63)]
+
+
+@pytest.mark.parametrize("dtype,op", [("bf16", "avg"), ("bf16", "sum"), ("fp32", "sum"), ("fp32", "avg"),
+                                      ("int32", "sum")])
+@pytest.mark.parametrize("N,S", AR_SHAPES)
+@pytest.mark.parametrize("order", ["ring", "rank"])
+def test_all_reduce(dtype, op, N, S, order):
+    xs = _gen(dtype, N, S, seed=N * 7 + S)
+    want = C.all_reduce(xs, dtype, op, order)[0] if S else np.zeros(0)
+    send = [to_dev(x, dtype) for x in xs]
+    for algo in ("fused", "rs_ag"):
+        recv = [empty(S, dtype) for _ in range(N)]
+        scratch = torch.empty(max(1, gc.gc_all_reduce_scratch_bytes(S, N, dtype)), dtype=torch.uint8, device=DEV)
+        gc.gc_all_reduce(send, recv, op=op, order=order, algo=algo, scratch=scratch)
+        torch.cuda.synchronize()
+        for r in range(N):
+            _check(from_dev(recv[r]), want, dtype, f"{algo} rank {r}")
+        for r in range(N):                                       # inputs untouched
+            assert_same(from_dev(send[r]), xs[r], dtype, "send modified")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("N", [2, 8])
+def test_all_reduce_in_place(dtype, N):
+    S = 4096 * 5 + 3
+    xs = _gen(dtype, N, S, seed=11)
+    want = C.all_reduce(xs, dtype, "avg", "ring")[0]
+    for algo in ("fused", "rs_ag"):
+        bufs = [to_dev(x, dtype) for x in xs]
+        scratch = torch.empty(gc.gc_all_reduce_scratch_bytes(S, N, dtype), dtype=torch.uint8, device=DEV)
+        gc.gc_all_reduce(bufs, None, op="avg", algo=algo, scratch=scratch)
+        torch.cuda.synchronize()
+        for r in range(N):
+            _check(from_dev(bufs[r]), want, dtype, f"in place {algo}")
+
+
+@pytest.mark.parametrize("offsets", [(1, 1, 1, 1), (3, 3, 3, 3), (0, 1, 2, 3), (5, 0, 5, 0)])
+def test_all_reduce_misaligned_views(offsets):
+    # views starting k elements into a larger allocation: a common phase keeps
+    # the vector path (with unaligned chunk edges); differing phases fall back
+    # to the element-wise kernel
+    N, S, dtype = 4, 10000 + 17, "bf16"
+    xs = _gen(dtype, N, S, seed=5)
+    want = C.all_reduce(xs, dtype, "avg", "ring")[0]
+    base_in = [empty(S + 8, dtype) for _ in range(N)]
+    base_out = [empty(S + 8, dtype) for _ in range(N)]
+    send = [b[o:o + S] for b, o in zip(base_in, offsets)]
+    recv = [b[o:o + S] for b, o in zip(base_out, offsets)]
+    for v, x in zip(send, xs):
+        v.copy_(to_dev(x, dtype))
+    gc.gc_all_reduce(send, recv, op="avg")
+    torch.cuda.synchronize()
+    for r in range(N):
+        _check(from_dev(recv[r]), want, dtype, f"offsets {offsets}")
+
+
+def test_all_reduce_fused_equals_rs_ag_bitwise():
+    # all-reduce == all-gather(reduce-scatter(x)) on the device, called as separate entry points
+    N, rc, dtype = 8, 4096 + 8, "bf16"
+    S = N * rc
+    xs = _gen(dtype, N, S, seed=9)
+    send = [to_dev(x, dtype) for x in xs]
+    ar = [empty(S, dtype) for _ in range(N)]
+    gc.gc_all_reduce(send, ar, op="avg")
+    shards = [empty(rc, dtype) for _ in range(N)]
+    gc.gc_reduce_scatter(send, shards, op="avg")
+    ag = [empty(S, dtype) for _ in range(N)]
+    gc.gc_all_gather(shards, ag)
+    torch.cuda.synchronize()
+    for r in range(N):
+        assert torch.equal(ar[r].view(torch.int16), ag[r].view(torch.int16))
+
+
+# ------------------------------------------------------------------ reduce-scatter
+
+@pytest.mark.parametrize("tin,tout,op", [("bf16", "fp32", "avg"), ("bf16", "bf16", "avg"), ("fp32", "fp32", "sum"),
+                                         ("fp32", "bf16", "avg"), ("int32", "int32", "sum")])
+@pytest.mark.parametrize("N,rc", [(1, 7), (2, 1), (3, 1000), (4, 5), (8, 4096 + 3), (64, 700), (64, 8)])
+@pytest.mark.parametrize("order", ["ring", "rank"])
+def test_reduce_scatter(tin, tout, op, N, rc, order):
+    xs = _gen(tin, N, N * rc, seed=N + rc)
+    want = C.reduce_scatter(xs, tin, tout, op, order)
+    send = [to_dev(x, tin) for x in xs]
+    recv = [empty(rc, tout) for _ in range(N)]
+    gc.gc_reduce_scatter(send, recv, op=op, order=order)
+    torch.cuda.synchronize()
+    for j in range(N):
+        _check(from_dev(recv[j]), want[j], tout, f"owner {j}")
+
+
+def test_reduce_scatter_in_place():
+    N, rc, dtype = 4, 3000, "bf16"
+    xs = _gen(dtype, N, N * rc, seed=3)
+    want = C.reduce_scatter(xs, dtype, dtype, "avg", "ring")
+    bufs = [to_dev(x, dtype) for x in xs]
+    recv = [bufs[r][r * rc:(r + 1) * rc] for r in range(N)]
+    gc.gc_reduce_scatter(bufs, recv, op="avg")
+    torch.cuda.synchronize()
+    for j in range(N):
+        _check(from_dev(recv[j]), want[j], dtype, f"in-place owner {j}")
+
+
+# ------------------------------------------------------------------ all-gather
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32", "int32"])
+@pytest.mark.parametrize("N,count", [(1, 9), (2, 1), (3, 1001), (8, 4096 * 2 + 1), (8, 8), (64, 513)])
+def test_all_gather(dtype, N, count):
+    shards = _gen(dtype, N, count, seed=N * count)
+    want = C.all_gather(shards)
+    send = [to_dev(x, dtype) for x in shards]
+    recv = [empty(N * count, dtype) for _ in range(N)]
+    gc.gc_all_gather(send, recv)
+    torch.cuda.synchronize()
+    for d in range(N):
+        assert_same(from_dev(recv[d]), want[d], dtype, f"rank {d}")
+
+
+def test_all_gather_in_place():
+    N, count, dtype = 8, 2049, "bf16"
+    shards = _gen(dtype, N, count, seed=1)
+    want = C.all_gather(shards)
+    recv = [empty(N * count, dtype) for _ in range(N)]
+    for r in range(N):
+        recv[r][r * count:(r + 1) * count].copy_(to_dev(shards[r], dtype))
+    send = [recv[r][r * count:(r + 1) * count] for r in range(N)]
+    gc.gc_all_gather(send, recv)
+    torch.cuda.synchronize()
+    for d in range(N):
+        assert_same(from_dev(recv[d]), want[d], dtype, f"in place rank {d}")
+
+
+# ------------------------------------------------------------------ special values
+
+def test_special_values_bf16_and_fp32():
+    N, S = 4, 4096 + 64
+    rng = np.random.default_rng(0)
+    specials = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, 1e-40, -1e-40, 3.0e38, -3.0e38,
+                         1.17549435e-38, 65504.0, 1.0 + 2 ** -8], np.float32)
+    xs32 = [rng.normal(size=S).astype(np.float32) for _ in range(N)]
+    for r in range(N):
+        pos = rng.choice(S, size=200, replace=False)
+        xs32[r][pos] = rng.choice(specials, size=200)
+    # a column of -0.0 everywhere: the fold starts from the first operand, so -0.0 survives
+    for r in range(N):
+        xs32[r][17] = -0.0
+    for dtype in ("fp32", "bf16"):
+        xs = xs32 if dtype == "fp32" else [f32_to_bf16(x) for x in xs32]
+        for op in ("sum", "avg"):
+            want = C.all_reduce(xs, dtype, op, "ring")[0]
+            send = [to_dev(x, dtype) for x in xs]
+            recv = [empty(S, dtype) for _ in range(N)]
+            gc.gc_all_reduce(send, recv, op=op)
+            torch.cuda.synchronize()
+            _check(from_dev(recv[0]), want, dtype, f"special {dtype} {op}")
+
+
+def test_subnormal_results_not_flushed():
+    # sums and averages landing in the fp32 / bf16 subnormal range
+    N, S = 8, 2048
+    tiny = np.float32(2.0 ** -133)
+    xs = [np.full(S, tiny * (r + 1), np.float32) for r in range(N)]
+    for dtype in ("fp32", "bf16"):
+        ins = xs if dtype == "fp32" else [f32_to_bf16(x) for x in xs]
+        want = C.all_reduce(ins, dtype, "avg", "ring")[0]
+        send = [to_dev(x, dtype) for x in ins]
+        recv = [empty(S, dtype) for _ in range(N)]
+        gc.gc_all_reduce(send, recv, op="avg")
+        torch.cuda.synchronize()
+        got = from_dev(recv[0])
+        _check(got, want, dtype, "subnormal")
+        assert np.all(got != 0)
+
+
+# ------------------------------------------------------------------ all-to-all
+
+def _a2a_case(N, E, row_bytes, seed, max_rows=5, zero_frac=0.2):
+    rng = np.random.default_rng(seed)
+    splits = rng.integers(0, max_rows + 1, size=(N, N, E)).astype(np.int64)
+    splits[rng.random(splits.shape) < zero_frac] = 0
+    sends = [rng.integers(0, 256, size=int(splits[s].sum()) * row_bytes, dtype=np.uint8) for s in range(N)]
+    return splits, sends
+
+
+@pytest.mark.parametrize("N,E,row_bytes", [(2, 1, 16), (3, 2, 48), (4, 1, 6), (8, 8, 8192), (8, 8, 16),
+                                           (5, 3, 1), (16, 8, 32), (8, 1, 4100)])
+def test_all_to_all(N, E, row_bytes):
+    splits, sends = _a2a_case(N, E, row_bytes, seed=N * E + row_bytes)
+    want = C.all_to_all(sends, splits, row_bytes)
+    send = [torch.from_numpy(s).to(DEV) if s.size else torch.empty(1, dtype=torch.uint8, device=DEV) for s in sends]
+    recv = [torch.full((max(1, len(w)),), 7, dtype=torch.uint8, device=DEV) for w in want]
+    gc.gc_all_to_all(send, recv, splits, row_bytes)
+    torch.cuda.synchronize()
+    for d in range(N):
+        got = recv[d].cpu().numpy()[:len(want[d])]
+        assert np.array_equal(got, want[d]), f"rank {d}"
+
+
+def test_all_to_all_skewed_single_destination():
+    # every row to rank 0, expert 0: one hot destination
+    N, E, rb = 8, 8, 256
+    splits = np.zeros((N, N, E), dtype=np.int64)
+    splits[:, 0, 0] = 300
+    rng = np.random.default_rng(4)
+    sends = [rng.integers(0, 256, size=300 * rb, dtype=np.uint8) for _ in range(N)]
+    want = C.all_to_all(sends, splits, rb)
+    send = [torch.from_numpy(s).to(DEV) for s in sends]
+    recv = [torch.zeros(max(1, len(w)), dtype=torch.uint8, device=DEV) for w in want]
+    gc.gc_all_to_all(send, recv, splits, rb)
+    torch.cuda.synchronize()
+    assert np.array_equal(recv[0].cpu().numpy(), want[0])
+
+
+# ------------------------------------------------------------------ bucket pack / unpack
+
+@pytest.mark.parametrize("dtype,cap,pad,seed", [("bf16", 40, 1, 0), ("bf16", 1 << 20, 8, 1), ("fp32", 1, 1, 2),
+                                               ("fp32", 200, 3, 3), ("bf16", 3000, 1, 4)])
+def test_bucket_pack_unpack(dtype, cap, pad, seed):
+    rng = np.random.default_rng(seed)
+    N = 3
+    numels = [int(x) for x in rng.integers(0, 700, size=12)] + [4096 * 3 + 5, 1, 0]
+    T = len(numels)
+    host = [[_gen(dtype, 1, n, seed=seed * 100 + r * 17 + t)[0] for t, n in enumerate(numels)] for r in range(N)]
+    dev = [[to_dev(host[r][t], dtype) if numels[t] else empty(1, dtype) for t in range(T)] for r in range(N)]
+    plan = gc.BucketPlan(numels, dtype, cap * ELEM[dtype], reverse=True, pad_to=pad)
+    want_buckets = OB.assign_buckets(numels, ELEM[dtype], cap * ELEM[dtype], reverse=True)
+    assert plan.nbuckets == len(want_buckets)
+    flat_tensors = [dev[r][t] for r in range(N) for t in range(T)]
+    outs = [[empty(numels[t] if numels[t] else 1, dtype) for t in range(T)] for r in range(N)]
+    flat_outs = [outs[r][t] for r in range(N) for t in range(T)]
+    for b, ts in enumerate(want_buckets):
+        bufs = [torch.full((max(1, plan.bucket_numel[b]),), 77, dtype=gc_torch(dtype), device=DEV)
+                for _ in range(N)]
+        plan.pack(b, flat_tensors, bufs, N)
+        plan.unpack(b, bufs, flat_outs, N)
+        torch.cuda.synchronize()
+        for r in range(N):
+            want = OB.pack(host[r], ts, numels, pad_to=pad)
+            assert_same(from_dev(bufs[r])[:len(want)], want, dtype, f"bucket {b} rank {r}")
+            for t in ts:
+                if numels[t]:
+                    assert_same(from_dev(outs[r][t]), host[r][t], dtype, f"unpack {t}")
+
+
+def gc_torch(dtype):
+    return {"bf16": torch.bfloat16, "fp32": torch.float32, "int32": torch.int32}[dtype]
+
+
+def test_pack_misaligned_segments():
+    # tensors at odd element offsets inside larger allocations: the copy kernel
+    # falls back to narrow accesses where source and destination disagree mod 16
+    N, dtype = 2, "bf16"
+    numels = [1001, 3, 4096 + 7, 9]
+    T = len(numels)
+    host = [[_gen(dtype, 1, n, seed=r * 10 + t)[0] for t, n in enumerate(numels)] for r in range(N)]
+    bases = [[empty(n + 8, dtype) for n in numels] for _ in range(N)]
+    views = [[bases[r][t][1 + t:1 + t + numels[t]] for t in range(T)] for r in range(N)]
+    for r in range(N):
+        for t in range(T):
+            views[r][t].copy_(to_dev(host[r][t], dtype))
+    plan = gc.BucketPlan(numels, dtype, 1 << 30, reverse=False)
+    bufs = [empty(plan.bucket_numel[0], dtype) for _ in range(N)]
+    plan.pack(0, [views[r][t] for r in range(N) for t in range(T)], bufs, N)
+    torch.cuda.synchronize()
+    for r in range(N):
+        assert_same(from_dev(bufs[r]), OB.pack(host[r], list(range(T)), numels), dtype, "misaligned pack")
+
+
+# ------------------------------------------------------------------ generator twin
+
+def test_device_generator_matches_host():
+    from gen import device as GD
+    n = 1 << 20
+    for r in (0, 3):
+        key = G.stream_key(7, r, 1)
+        t = GD.fill_uniform_f32(torch.empty(n, dtype=torch.float32, device=DEV), key, base=123)
+        assert np.array_equal(t.cpu().numpy().view(np.uint32), G.uniform_f32(key, np.arange(n) + 123).view(np.uint32))
+        t = GD.fill_normal_bf16(torch.empty(n, dtype=torch.bfloat16, device=DEV), key, 1e-3, base=5)
+        assert np.array_equal(from_dev(t), G.normal_bf16(key, np.arange(n) + 5, 1e-3))
+        t = GD.fill_int32(torch.empty(n, dtype=torch.int32, device=DEV), key)
+        assert np.array_equal(t.cpu().numpy(), G.int32_values(key, np.arange(n)))
+    tokens = np.array([5, 0, 77, 5, 1023], dtype=np.int32)
+    H = 96
+    key = G.stream_key(0, 2, 0)
+    t = GD.fill_normal_bf16_rows(torch.empty(len(tokens) * H, dtype=torch.bfloat16, device=DEV),
+                                 torch.from_numpy(tokens).to(DEV), H, key, 1.0)
+    want = np.concatenate([G.normal_bf16(key, tok * H + np.arange(H), 1.0) for tok in tokens])
+    assert np.array_equal(from_dev(t), want)
