@@ -1,0 +1,454 @@
+"""Benchmark of the gradient-sync collectives on one MI355X.
+
+Default: the all-reduce the headline metric is quoted on, 8 ranks x 33,554,432
+bf16 elements (64 MiB each), averaged in fp32, rounded to bf16, ring fold
+order, fused single-pass kernel.  One step = one all-reduce of one batch of
+rank buffers.  Inputs are generated on the device (seeded, synthetic) before
+the timed region and rotated over several replicas so that consecutive steps
+never find their data in the 256 MB MALL.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Prints one JSON line.  value = algorithmic bytes per step / time per step
+(every input read once, every output written once), in GB/s; roofline.frac
+is the dominant kernel's achieved bandwidth over the 8 TB/s HBM3E peak.
+
+Other workloads (--workload): ar_fp32_n4, ddp_llama7b, fsdp_layer_n64,
+moe_a2a_n8 (the remaining parity configurations, measured the same way).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective HBM GB/s (% of peak) for N=8 × 64 MiB bf16 all-reduce on 1 MI355X"
+KERNEL_SOURCES = ["collective_communication_reduction_amd/csrc/reduce.hip",
+                  "collective_communication_reduction_amd/csrc/movement.hip",
+                  "collective_communication_reduction_amd/csrc/device_common.h"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="ar_bf16_n8",
+                   choices=["ar_bf16_n8", "ar_fp32_n4", "ddp_llama7b", "fsdp_layer_n64", "moe_a2a_n8"])
+    p.add_argument("--replicas", type=int, default=4)
+    p.add_argument("--layout", default="staggered", choices=["staggered", "separate"],
+                   help="placement of the rank buffers in HBM")
+    p.add_argument("--stagger", type=int, default=4096, help="bytes between rank slots (staggered layout)")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="also launch a plain device copy of this many MiB (counter calibration runs)")
+    return p.parse_args()
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per launch of the dominant kernel, from the committed counter
+    summary, if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    m = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not m or not t or m.group(1) != kernel_hash():
+        return None
+    return int(t.group(1))
+
+
+# ----------------------------------------------------------------- workloads
+
+class Workload:
+    """Device buffers plus one step's launches; algorithmic bytes per step."""
+    name = ""
+    bytes_per_step = 0
+    dominant = ""
+    dominant_bytes = 0
+
+    def step(self, k):
+        raise NotImplementedError
+
+    def dominant_launch(self, k):
+        """Launch only the dominant kernel of step k (for its per-launch timing)."""
+        self.step(k)
+
+
+def rank_buffers(args, nranks, count, tdt):
+    """Rank buffers in HBM: one slab with a 4 KiB per-rank stagger (default), or separate allocations."""
+    import torch
+    import collective_communication_reduction_amd as gc
+    if args.layout == "separate":
+        return [torch.empty(count, dtype=tdt, device="cuda") for _ in range(nranks)]
+    return gc.gc_rank_buffers(nranks, count, tdt, stagger_bytes=args.stagger)
+
+
+def layout_name(args):
+    return "separate allocations" if args.layout == "separate" else f"one slab, {args.stagger} B stagger per rank"
+
+
+def _keyed(seed, r, stream=0):
+    from gen.host import stream_key
+    return stream_key(seed, r, stream)
+
+
+class AllReduceWorkload(Workload):
+    def __init__(self, args, nranks, count, dtype, op):
+        import torch
+        import collective_communication_reduction_amd as gc
+        from gen import device as GD
+        self.gc = gc
+        self.N, self.S, self.dtype, self.op = nranks, count, dtype, op
+        tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+        es = 2 if dtype == "bf16" else 4
+        self.name = f"ar_{dtype}_n{nranks}"
+        self.bytes_per_step = 2 * nranks * count * es
+        self.dominant = "reduce_vec_kernel (fused all-reduce)"
+        self.dominant_bytes = self.bytes_per_step
+        self.sets = []
+        self.layout = layout_name(args)
+        for rep in range(args.replicas):
+            send = rank_buffers(args, nranks, count, tdt)
+            recv = rank_buffers(args, nranks, count, tdt)
+            for r, t in enumerate(send):
+                if dtype == "bf16":
+                    GD.fill_normal_bf16(t, _keyed(args.seed, r), 1e-3)
+                else:
+                    GD.fill_uniform_f32(t, _keyed(args.seed, r))
+            self.sets.append((send, recv))
+        torch.cuda.synchronize()
+
+    def step(self, k):
+        send, recv = self.sets[k % len(self.sets)]
+        self.gc.gc_all_reduce(send, recv, op=self.op, order="ring", algo="fused")
+
+    def config(self):
+        return {"workload": self.name, "nranks": self.N, "count_per_rank": self.S, "storage": self.dtype,
+                "op": self.op, "order": "ring", "algo": "fused", "replicas": len(self.sets), "layout": self.layout}
+
+    def cpu_sample(self, seed):
+        """Oracle all-reduce on the first quarter of every rank's buffer."""
+        import numpy as np
+        from gen import host as G
+        from oracle import collectives as C
+        S = self.S // 4
+        xs = []
+        for r in range(self.N):
+            key = _keyed(seed, r)
+            xs.append(G.normal_bf16(key, np.arange(S), 1e-3) if self.dtype == "bf16" else
+                      G.uniform_f32(key, np.arange(S)))
+        es = 2 if self.dtype == "bf16" else 4
+        return (lambda: C.all_reduce(xs, self.dtype, self.op, "ring"), 2 * self.N * S * es,
+                f"oracle ring all-reduce of {self.N} ranks x {S} {self.dtype} (first quarter of each buffer)")
+
+
+class DdpWorkload(Workload):
+    """Llama-7B gradient set, 8 ranks, 25 MiB buckets: pack -> fused all-reduce (avg) -> unpack per bucket."""
+
+    def __init__(self, args):
+        import torch
+        import collective_communication_reduction_amd as gc
+        from gen import device as GD
+        from gen.workloads import WORKLOADS, llama7b_tensors
+        self.gc = gc
+        cfg = WORKLOADS["ddp_llama7b"]
+        self.N = cfg["nranks"]
+        self.name = "ddp_llama7b"
+        numels = [n for _, n in llama7b_tensors()]
+        self.numels = numels
+        self.plan = gc.BucketPlan(numels, "bf16", cfg["cap_bytes"], reverse=True)
+        total = sum(numels)
+        # one flat allocation per rank; tensor t is a view at its model-order offset
+        self.flat = rank_buffers(args, self.N, total, torch.bfloat16)
+        self.layout = layout_name(args)
+        offs, run = [], 0
+        for n in numels:
+            offs.append(run)
+            run += n
+        for r in range(self.N):
+            GD.fill_normal_bf16(self.flat[r], _keyed(args.seed, r), cfg["sigma"])
+        self.tensors = [self.flat[r][o:o + n] for r in range(self.N) for o, n in zip(offs, numels)]
+        big = max(self.plan.bucket_numel)
+        self.bufs = [rank_buffers(args, self.N, big, torch.bfloat16) for _ in range(2)]
+        self.bucket_bytes = [b * 2 for b in self.plan.bucket_numel]
+        self.bytes_per_step = 6 * self.N * sum(self.bucket_bytes)
+        self.dominant = "reduce_vec_kernel (fused all-reduce of each bucket)"
+        self.dominant_bytes = 2 * self.N * sum(self.bucket_bytes)
+        torch.cuda.synchronize()
+
+    def step(self, k):
+        gc, plan, N = self.gc, self.plan, self.N
+        for b in range(plan.nbuckets):
+            bufs = self.bufs[b & 1]
+            n = plan.bucket_numel[b]
+            views = [x[:n] for x in bufs]
+            plan.pack(b, self.tensors, views, N)
+            gc.gc_all_reduce(views, views, op="avg", order="ring", algo="fused")
+            plan.unpack(b, views, self.tensors, N)
+
+    def dominant_launch(self, k):
+        plan = self.plan
+        for b in range(plan.nbuckets):
+            views = [x[:plan.bucket_numel[b]] for x in self.bufs[b & 1]]
+            self.gc.gc_all_reduce(views, views, op="avg", order="ring", algo="fused")
+
+    def config(self):
+        return {"workload": self.name, "nranks": self.N, "params": sum(self.numels), "storage": "bf16",
+                "buckets": self.plan.nbuckets, "cap_bytes": 25 * 1024 * 1024, "op": "avg", "order": "ring",
+                "layout": self.layout}
+
+    def cpu_sample(self, seed):
+        import numpy as np
+        from gen import host as G
+        from oracle import buckets as OB
+        from oracle import collectives as C
+        b = 1  # [final_norm, L31 norms, L31 down_proj]: a mixed bucket
+        ts = OB.assign_buckets(self.numels, 2, 25 * 1024 * 1024, reverse=True)[b]
+        offs = np.cumsum([0] + self.numels)
+        n_per = 1 << 20  # first 1 Mi elements of each tensor of the bucket
+        numels = [min(self.numels[t], n_per) for t in ts]
+        per_rank = []
+        for r in range(self.N):
+            key = _keyed(seed, r)
+            per_rank.append([G.normal_bf16(key, offs[t] + np.arange(n), 1e-3) for t, n in zip(ts, numels)])
+        idx = list(range(len(ts)))
+
+        def run():
+            flats = [OB.pack(per_rank[r], idx, numels) for r in range(self.N)]
+            out = C.all_reduce(flats, "bf16", "avg", "ring")
+            return [OB.unpack(out[r], idx, numels) for r in range(self.N)]
+        nbytes = 6 * self.N * sum(numels) * 2
+        return run, nbytes, f"oracle pack + ring all-reduce + unpack of bucket {b} truncated to {sum(numels)} elements"
+
+
+class FsdpWorkload(Workload):
+    """One transformer layer flattened, 64 ranks: reduce-scatter (avg) bf16 -> fp32, then all-gather bf16."""
+
+    def __init__(self, args):
+        import torch
+        import collective_communication_reduction_amd as gc
+        from gen import device as GD
+        from gen.workloads import fsdp_layer_tensors
+        self.gc = gc
+        self.N = 64
+        self.name = "fsdp_layer_n64"
+        total = sum(n for _, n in fsdp_layer_tensors())
+        self.S = -(-total // self.N) * self.N
+        self.rc = self.S // self.N
+        self.grads = rank_buffers(args, self.N, self.S, torch.bfloat16)
+        self.gshards = rank_buffers(args, self.N, self.rc, torch.float32)
+        self.pshards = rank_buffers(args, self.N, self.rc, torch.bfloat16)
+        self.params = rank_buffers(args, self.N, self.S, torch.bfloat16)
+        self.layout = layout_name(args)
+        for r in range(self.N):
+            GD.fill_normal_bf16(self.grads[r], _keyed(args.seed, r, 0), 1e-3)
+            GD.fill_normal_bf16(self.pshards[r], _keyed(args.seed, r, 1), 0.02)
+        self.rs_bytes = self.N * self.S * 2 + self.N * self.rc * 4
+        self.ag_bytes = self.N * self.rc * 2 + self.N * self.S * 2
+        self.bytes_per_step = self.rs_bytes + self.ag_bytes
+        self.dominant = "reduce_vec_kernel (reduce-scatter, 64 ranks)"
+        self.dominant_bytes = self.rs_bytes
+        torch.cuda.synchronize()
+
+    def step(self, k):
+        self.gc.gc_reduce_scatter(self.grads, self.gshards, op="avg", order="ring")
+        self.gc.gc_all_gather(self.pshards, self.params)
+
+    def dominant_launch(self, k):
+        self.gc.gc_reduce_scatter(self.grads, self.gshards, op="avg", order="ring")
+
+    def config(self):
+        return {"workload": self.name, "nranks": self.N, "flat_numel": self.S, "shard": self.rc,
+                "rs": "bf16->fp32 avg ring", "ag": "bf16", "layout": self.layout}
+
+    def cpu_sample(self, seed):
+        import numpy as np
+        from gen import host as G
+        from oracle import sampled as SM
+        m = 1 << 17  # 131072 sampled outputs of owner 5
+
+        vals = np.stack([G.normal_bf16(_keyed(seed, i, 0), 5 * self.rc + np.arange(m), 1e-3) for i in range(self.N)])
+
+        def run():
+            return SM.reduce_scatter_at(vals, np.full(m, 5), np.arange(m), self.rc, "bf16", "fp32", "avg", "ring")
+        return run, self.N * m * 2 + m * 4, f"oracle reduce-scatter of {m} outputs of owner 5 (64-way fold each)"
+
+
+class MoeWorkload(Workload):
+    """MoE dispatch all-to-all, 8 ranks x 16384 tokens x 4096 bf16, top-2 of 64 experts, Zipf(1.1)."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+        import collective_communication_reduction_amd as gc
+        from gen import device as GD
+        from gen.workloads import WORKLOADS, moe_send_layout
+        self.gc = gc
+        cfg = WORKLOADS["moe_a2a_n8"]
+        self.N, self.H = cfg["nranks"], cfg["hidden"]
+        self.name = "moe_a2a_n8"
+        self.splits, rows = moe_send_layout(args.seed, self.N, cfg["tokens"], cfg["experts"], cfg["topk"],
+                                            cfg["zipf_s"])
+        self.row_bytes = self.H * 2
+        self.send = []
+        for s in range(self.N):
+            t = torch.empty(len(rows[s]) * self.H, dtype=torch.bfloat16, device="cuda")
+            GD.fill_normal_bf16_rows(t, torch.from_numpy(rows[s]).cuda(), self.H, _keyed(args.seed, s), 1.0)
+            self.send.append(t)
+        recv_rows = self.splits.sum(axis=(0, 2))
+        self.recv = [torch.empty(int(n) * self.H, dtype=torch.bfloat16, device="cuda") for n in recv_rows]
+        total_rows = int(self.splits.sum())
+        self.bytes_per_step = 2 * total_rows * self.row_bytes
+        self.dominant = "a2a_kernel"
+        self.dominant_bytes = self.bytes_per_step
+        self.frac_dst0 = float(self.splits[:, 0, :].sum() / total_rows)
+        self.rows = rows
+        torch.cuda.synchronize()
+
+    def step(self, k):
+        self.gc.gc_all_to_all(self.send, self.recv, self.splits, self.row_bytes)
+
+    def config(self):
+        return {"workload": self.name, "nranks": self.N, "tokens": 16384, "hidden": self.H, "experts": 64,
+                "topk": 2, "zipf_s": 1.1, "rows": int(self.splits.sum()), "frac_rows_to_rank0": round(self.frac_dst0, 4)}
+
+    def cpu_sample(self, seed):
+        import numpy as np
+        from gen import host as G
+        from oracle import collectives as C
+        # the full routing, with 256-element rows (the first 256 of the 4096 hidden values)
+        h = 256
+        sends = [np.concatenate([G.normal_bf16(_keyed(seed, s), tok * self.H + np.arange(h), 1.0)
+                                 for tok in self.rows[s][:4096]]) for s in range(self.N)]
+        # keep the splits consistent with the truncated row lists: first 4096 rows of each source
+        sub = np.zeros_like(self.splits)
+        for s in range(self.N):
+            left = 4096
+            for d in range(self.N):
+                for e in range(self.splits.shape[2]):
+                    take = min(left, int(self.splits[s, d, e]))
+                    sub[s, d, e] = take
+                    left -= take
+
+        def run():
+            return C.all_to_all(sends, sub, h)
+        return run, 2 * int(sub.sum()) * h * 2, "oracle all-to-all of the first 4096 rows of each source, 256 of 4096 columns"
+
+
+def make(args):
+    if args.workload in ("ar_bf16_n8", "ar_fp32_n4"):
+        from gen.workloads import WORKLOADS
+        c = WORKLOADS[args.workload]
+        return AllReduceWorkload(args, c["nranks"], c["count"], c["dtype"], c["op"])
+    if args.workload == "ddp_llama7b":
+        return DdpWorkload(args)
+    if args.workload == "fsdp_layer_n64":
+        return FsdpWorkload(args)
+    return MoeWorkload(args)
+
+
+# ----------------------------------------------------------------- timing
+
+def time_steps(fn, steps, warmup):
+    """HIP events on torch's current stream (the stream every libgc launch uses)."""
+    import torch
+    for k in range(warmup):
+        fn(k)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(steps):
+        fn(warmup + k)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step
+
+
+def cpu_baseline(w, seed):
+    run, nbytes, what = w.cpu_sample(seed)
+    run()  # warm the code paths once (numpy allocations)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        run()
+        reps += 1
+        if time.perf_counter() - t0 >= 10.0 or reps >= 20:
+            break
+    per = (time.perf_counter() - t0) / reps
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what}; {reps} runs, {per:.3f} s each, single-threaded numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs all N ranks as buffers in one MI355X's HBM "
+              f"(no collectives across GPUs), so --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.init()
+    w = make(args)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    ms = time_steps(w.step, args.steps, args.warmup)
+    if type(w).dominant_launch is Workload.dominant_launch:
+        kms = ms
+        launches = 1
+    else:
+        kms = time_steps(w.dominant_launch, max(3, args.steps // 5), 2)
+        launches = 1
+    value = w.bytes_per_step / (ms * 1e-3) / 1e9
+    achieved = w.dominant_bytes / (kms * 1e-3) / 1e9 / launches
+    traffic = traffic_from_profiles(w.name)
+    out = {
+        "metric": METRIC if w.name == "ar_bf16_n8" else f"effective HBM GB/s for {w.name} on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": w.config(),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": w.dominant, "algorithmic_bytes_per_launch": w.dominant_bytes},
+        "bytes_per_step": w.bytes_per_step,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.seed)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

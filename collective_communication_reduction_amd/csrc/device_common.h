@@ -11,18 +11,41 @@ namespace gcdev {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;  // four 64-wide wavefronts per workgroup
+#ifndef GC_THREADS
+#define GC_THREADS 256
+#endif
+constexpr int kThreads = GC_THREADS;  // 64-wide wavefronts per workgroup: kThreads / 64
+
+// Build-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef GC_NT_LOAD
+#define GC_NT_LOAD 1
+#endif
+#ifndef GC_NT_STORE
+#define GC_NT_STORE 1
+#endif
 
 // Streaming data is touched exactly once per launch, so loads and stores carry
 // the non-temporal hint: they should not displace other data in L2 / MALL.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
+#if GC_NT_LOAD
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
+#if GC_NT_STORE
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+#else
+  *reinterpret_cast<u32x4*>(p) = v;
+#endif
 }
 __device__ __forceinline__ void st8(void* p, u32x2 v) {
+#if GC_NT_STORE
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+#else
+  *reinterpret_cast<u32x2*>(p) = v;
+#endif
 }
 
 // ---------------------------------------------------------------- inputs

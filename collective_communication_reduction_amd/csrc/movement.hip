@@ -108,6 +108,7 @@ __global__ void __launch_bounds__(kThreads) segment_narrow_kernel(const SegArgs 
 // ------------------------------------------------------------ all-to-all
 
 constexpr int kA2AMax = gci::kA2AMaxBlocks;
+static_assert(2 * kThreads >= kA2AMax, "the block scans hold two entries per thread");
 
 struct A2AArgs {
   const char* send[GC_MAX_RANKS];

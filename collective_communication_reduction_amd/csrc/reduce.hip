@@ -396,7 +396,14 @@ __global__ void __launch_bounds__(kThreads) gather_elem_kernel(const RedArgs<P> 
 
 // ------------------------------------------------------------------ host side
 
-constexpr uint32_t kMaxGrid = 1u << 20;
+#ifndef GC_RED_MAX_GRID
+#define GC_RED_MAX_GRID (1u << 20)
+#endif
+#ifndef GC_RED_U
+#define GC_RED_U 2
+#endif
+
+constexpr uint32_t kMaxGrid = GC_RED_MAX_GRID;
 
 uint64_t addr(const void* p) { return reinterpret_cast<uint64_t>(p); }
 
@@ -482,7 +489,7 @@ gc_status dispatch_reduce(const gci::ReduceCall& c, const Plan& pl) {
   return launch(reduce_vec_kernel<KIND, In, Out, 0, U, GC_MAX_RANKS>, a, ntiles, c.stream);
 }
 
-constexpr int kU = 2;
+constexpr int kU = GC_RED_U;
 
 template <int KIND, class In, class Out>
 gc_status run_reduce(const gci::ReduceCall& c) {

@@ -157,3 +157,14 @@ def test_bucket_pack_validation():
     assert _status(plan.unpack, 0, bufs, tensors, 0, stream=0) == gc.GC_ERR_INVALID_ARG
     with pytest.raises(gc.GcError):
         gc.gc_bucket_plan_create([1, 2], "bf16", 10, pad_to=0)
+
+
+def test_rank_buffers_layout():
+    # host tensors stand in for device memory: only the offsets are checked
+    bufs = gc.gc_rank_buffers(8, 1000, "bf16", device="cpu", stagger_bytes=4096, slot_align=1 << 20)
+    base = bufs[0].data_ptr()
+    for r, b in enumerate(bufs):
+        assert b.numel() == 1000 and b.is_contiguous()
+        assert b.data_ptr() - base == r * ((1 << 20) + 4096)
+    with pytest.raises(ValueError):
+        gc.gc_rank_buffers(2, 10, "fp32", device="cpu", stagger_bytes=6)
