@@ -18,6 +18,7 @@ def mix64(z):
 
 
 def stream_key(seed, rank, stream):
+    seed, rank, stream = int(seed), int(rank), int(stream)
     a = int(mix64(np.uint64((seed + rank) & MASK64)))
     b = int(mix64(np.uint64((stream + GOLDEN) & MASK64)))
     return (a ^ b) & MASK64

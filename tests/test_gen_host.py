@@ -46,3 +46,7 @@ def test_moe_routing_shape():
     assert 0.5 < frac0 < 0.7
     chosen = W.route_tokens(0, 0, 1024, 64, 2, 1.1)
     assert np.all(chosen[:, 0] != chosen[:, 1])
+
+
+def test_stream_key_accepts_numpy_integers():
+    assert G.stream_key(np.int64(0), np.int64(3), np.int32(1)) == G.stream_key(0, 3, 1)

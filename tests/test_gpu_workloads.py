@@ -1,0 +1,212 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration and
+HBM layout bench.py times (rank buffers in one slab, 4 KiB per-rank stagger).
+
+At these sizes the step-by-step oracle cannot hold the inputs, so each test
+checks (a) sampled outputs the oracle computes one by one from inputs it
+regenerates on the host by index (random positions plus every chunk edge),
+and (b) properties that hold at any size, checked on the device: every rank's
+result is identical, fused == reduce-scatter + all-gather bit for bit, and
+data movement equals the permutation the oracle derives.  The 4-rank fp32
+all-reduce is small enough for a full oracle comparison."""
+
+import numpy as np
+import pytest
+import torch
+
+import collective_communication_reduction_amd as gc
+from gen import device as GD
+from gen import host as G
+from gen.workloads import WORKLOADS, fsdp_layer_tensors, llama7b_tensors, moe_send_layout
+from oracle import buckets as OB
+from oracle import collectives as C
+from oracle import sampled as SM
+from tests.gpu_util import DEV, assert_same, from_dev, max_ulp
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _positions(S, N, rng, m=1 << 18):
+    """Random positions plus the first and last two elements of every owner chunk."""
+    c = -(-S // N)
+    edges = []
+    for j in range(N):
+        lo, hi = min(S, j * c), min(S, (j + 1) * c)
+        edges += [lo, lo + 1, hi - 2, hi - 1]
+    pos = np.concatenate([rng.integers(0, S, size=m), np.array(edges)])
+    pos = pos[(pos >= 0) & (pos < S)]
+    return np.unique(pos)
+
+
+def _gather(t, pos):
+    idx = torch.from_numpy(pos.astype(np.int64)).to(DEV)
+    return from_dev(t.index_select(0, idx))
+
+
+def test_ar_fp32_n4_full():
+    cfg = WORKLOADS["ar_fp32_n4"]
+    N, S = cfg["nranks"], cfg["count"]
+    xs = [G.uniform_f32(G.stream_key(SEED, r, 0), np.arange(S)) for r in range(N)]
+    want = C.all_reduce(xs, "fp32", "sum", "ring")[0]
+    send = gc.gc_rank_buffers(N, S, "fp32")
+    for r in range(N):
+        GD.fill_uniform_f32(send[r], G.stream_key(SEED, r, 0))
+    for algo in ("fused", "rs_ag"):
+        recv = gc.gc_rank_buffers(N, S, "fp32")
+        scratch = torch.empty(gc.gc_all_reduce_scratch_bytes(S, N, "fp32"), dtype=torch.uint8, device=DEV)
+        gc.gc_all_reduce(send, recv, op="sum", order="ring", algo=algo, scratch=scratch)
+        torch.cuda.synchronize()
+        for r in range(N):
+            assert_same(from_dev(recv[r]), want, "fp32", f"{algo} rank {r}")
+
+
+def test_ar_bf16_n8_full():
+    cfg = WORKLOADS["ar_bf16_n8"]
+    N, S, sigma = cfg["nranks"], cfg["count"], cfg["sigma"]
+    send = gc.gc_rank_buffers(N, S, "bf16")
+    keys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    for r in range(N):
+        GD.fill_normal_bf16(send[r], keys[r], sigma)
+    recv = gc.gc_rank_buffers(N, S, "bf16")
+    gc.gc_all_reduce(send, recv, op="avg", order="ring", algo="fused")
+    # the same all-reduce as reduce-scatter then all-gather, separately
+    recv2 = gc.gc_rank_buffers(N, S, "bf16")
+    scratch = torch.empty(gc.gc_all_reduce_scratch_bytes(S, N, "bf16"), dtype=torch.uint8, device=DEV)
+    gc.gc_all_reduce(send, recv2, op="avg", order="ring", algo="rs_ag", scratch=scratch)
+    torch.cuda.synchronize()
+    for r in range(N):
+        assert torch.equal(recv[r].view(torch.int16), recv[0].view(torch.int16)), f"rank {r} differs"
+        assert torch.equal(recv2[r].view(torch.int16), recv[0].view(torch.int16)), f"rs_ag rank {r} differs"
+    pos = _positions(S, N, np.random.default_rng(1))
+    vals = np.stack([G.normal_bf16(keys[r], pos, sigma) for r in range(N)])
+    want = SM.all_reduce_at(vals, pos, S, "bf16", "avg", "ring")
+    got = _gather(recv[3], pos)
+    assert max_ulp(got, want) <= 1
+    assert_same(got, want, "bf16", "sampled outputs")
+
+
+def _llama_layout():
+    numels = [n for _, n in llama7b_tensors()]
+    offs = np.concatenate([[0], np.cumsum(numels)]).astype(np.int64)
+    return numels, offs
+
+
+def test_ddp_llama7b_full_step():
+    cfg = WORKLOADS["ddp_llama7b"]
+    N, sigma, cap = cfg["nranks"], cfg["sigma"], cfg["cap_bytes"]
+    numels, offs = _llama_layout()
+    total = int(offs[-1])
+    keys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    flat = gc.gc_rank_buffers(N, total, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(flat[r], keys[r], sigma)
+    tensors = [flat[r][int(offs[t]):int(offs[t]) + numels[t]] for r in range(N) for t in range(len(numels))]
+    plan = gc.BucketPlan(numels, "bf16", cap, reverse=True)
+    bufs = [gc.gc_rank_buffers(N, max(plan.bucket_numel), "bf16") for _ in range(2)]
+    for b in range(plan.nbuckets):                      # one step, exactly as bench.py runs it
+        views = [x[:plan.bucket_numel[b]] for x in bufs[b & 1]]
+        plan.pack(b, tensors, views, N)
+        gc.gc_all_reduce(views, views, op="avg", order="ring", algo="fused")
+        plan.unpack(b, views, tensors, N)
+    torch.cuda.synchronize()
+    for r in range(1, N):
+        assert torch.equal(flat[r].view(torch.int16), flat[0].view(torch.int16)), f"rank {r} differs"
+    # sampled outputs of every bucket: bucket element e -> (tensor, index) -> model-order flat index
+    rng = np.random.default_rng(2)
+    oracle_buckets = OB.assign_buckets(numels, 2, cap, reverse=True)
+    assert plan.nbuckets == len(oracle_buckets)
+    flat_pos, want = [], []
+    for b, ts in enumerate(oracle_buckets):
+        boffs, used, _ = OB.bucket_layout(ts, numels)
+        e = np.unique(np.concatenate([rng.integers(0, used, size=48), [0, used - 1],
+                                      [min(used - 1, j * -(-used // N)) for j in range(N)]]))
+        starts = np.asarray(boffs)
+        which = np.searchsorted(starts, e, side="right") - 1
+        fidx = np.array([offs[ts[w]] + (ee - starts[w]) for w, ee in zip(which, e)], dtype=np.int64)
+        vals = np.stack([G.normal_bf16(keys[r], fidx, sigma) for r in range(N)])
+        want.append(SM.all_reduce_at(vals, e, used, "bf16", "avg", "ring"))
+        flat_pos.append(fidx)
+    flat_pos = np.concatenate(flat_pos)
+    want = np.concatenate(want)
+    got = _gather(flat[5], flat_pos)
+    assert max_ulp(got, want) <= 1
+    assert_same(got, want, "bf16", "sampled bucket outputs")
+    plan.close()
+
+
+def test_fsdp_layer_n64_full():
+    N = WORKLOADS["fsdp_layer_n64"]["nranks"]
+    numels = [n for _, n in fsdp_layer_tensors()]
+    _, used, S, _ = OB.flat_param_shards(numels, N)
+    rc = S // N
+    gkeys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    pkeys = [G.stream_key(SEED, r, 1) for r in range(N)]
+    grads = gc.gc_rank_buffers(N, S, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(grads[r], gkeys[r], 1e-3)
+    gshards = gc.gc_rank_buffers(N, rc, "fp32")
+    gc.gc_reduce_scatter(grads, gshards, op="avg", order="ring")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    for j in list(range(0, N, 7)) + [N - 1]:
+        k = np.unique(np.concatenate([rng.integers(0, rc, size=2048), [0, 1, rc - 2, rc - 1]]))
+        vals = np.stack([G.normal_bf16(gkeys[i], j * rc + k, 1e-3) for i in range(N)])
+        want = SM.reduce_scatter_at(vals, np.full(len(k), j), k, rc, "bf16", "fp32", "avg", "ring")
+        assert_same(_gather(gshards[j], k), want, "fp32", f"reduce-scatter owner {j}")
+    del grads, gshards
+    torch.cuda.empty_cache()
+    pshards = gc.gc_rank_buffers(N, rc, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(pshards[r], pkeys[r], 0.02)
+    params = gc.gc_rank_buffers(N, S, "bf16")
+    gc.gc_all_gather(pshards, params)
+    torch.cuda.synchronize()
+    for d in range(1, N):
+        assert torch.equal(params[d].view(torch.int16), params[0].view(torch.int16)), f"rank {d} differs"
+    pos = _positions(S, N, np.random.default_rng(4), m=1 << 16)
+    owner, k = pos // rc, pos % rc
+    want = np.array([G.normal_bf16(pkeys[i], np.array([kk]), 0.02)[0] for i, kk in zip(owner, k)], dtype=np.uint16)
+    assert_same(_gather(params[17], pos), want, "bf16", "all-gather sampled")
+
+
+def test_moe_a2a_n8_full():
+    cfg = WORKLOADS["moe_a2a_n8"]
+    N, H = cfg["nranks"], cfg["hidden"]
+    splits, rows = moe_send_layout(SEED, N, cfg["tokens"], cfg["experts"], cfg["topk"], cfg["zipf_s"])
+    send = []
+    for s in range(N):
+        t = torch.empty(len(rows[s]) * H, dtype=torch.bfloat16, device=DEV)
+        GD.fill_normal_bf16_rows(t, torch.from_numpy(rows[s]).to(DEV), H, G.stream_key(SEED, s, 0), 1.0)
+        send.append(t)
+    recv_rows = splits.sum(axis=(0, 2))
+    recv = [torch.empty(int(n) * H, dtype=torch.bfloat16, device=DEV) for n in recv_rows]
+    gc.gc_all_to_all(send, recv, splits, H * 2)
+    torch.cuda.synchronize()
+    # the oracle's permutation applied to global row ids gives every received row's source row
+    base = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    ids = [np.arange(base[s], base[s + 1], dtype=np.int64) for s in range(N)]
+    src_of = C.all_to_all(ids, splits, 1)
+    all_send = torch.cat(send).view(-1, H)
+    for d in range(N):
+        want = all_send.index_select(0, torch.from_numpy(src_of[d]).to(DEV))
+        assert torch.equal(recv[d].view(-1, H).view(torch.int16), want.view(torch.int16)), f"rank {d}"
+    # sampled rows against values the oracle regenerates from the routing alone
+    rng = np.random.default_rng(5)
+    for d in (0, 3, 7):
+        n = int(recv_rows[d])
+        pick = np.unique(np.concatenate([rng.integers(0, n, size=64), [0, n - 1]]))
+        srcs, srow = SM.a2a_source_rows(splits, d, pick)
+        want = np.stack([G.normal_bf16(G.stream_key(SEED, s, 0), int(rows[s][r]) * H + np.arange(H), 1.0)
+                         for s, r in zip(srcs, srow)])
+        got = from_dev(recv[d].view(-1, H).index_select(0, torch.from_numpy(pick).to(DEV)))
+        assert np.array_equal(got, want), f"rank {d} sampled rows"
+    # the skew the workload is meant to have: most rows land on rank 0
+    assert 0.55 < recv_rows[0] / recv_rows.sum() < 0.67
