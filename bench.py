@@ -125,7 +125,9 @@ class AllReduceWorkload(Workload):
         self.dominant_bytes = self.bytes_per_step
         self.sets = []
         self.layout = layout_name(args)
-        for rep in range(args.replicas):
+        # enough replica sets that one rotation touches >= 1 GiB (4x the 256 MB MALL)
+        reps = max(args.replicas, -(-(1 << 30) // self.bytes_per_step))
+        for rep in range(reps):
             send = rank_buffers(args, nranks, count, tdt)
             recv = rank_buffers(args, nranks, count, tdt)
             for r, t in enumerate(send):

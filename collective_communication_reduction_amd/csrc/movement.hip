@@ -253,7 +253,21 @@ __global__ void __launch_bounds__(kThreads) a2a_kernel(const A2AArgs a) {
 
 // ------------------------------------------------------------ host side
 
-constexpr uint32_t kMaxGrid = 1u << 20;
+#ifndef GC_SEG_MAX_GRID
+#define GC_SEG_MAX_GRID (1u << 20)
+#endif
+#ifndef GC_A2A_MAX_GRID
+#define GC_A2A_MAX_GRID (1u << 20)
+#endif
+#ifndef GC_A2A_TILE_BYTES
+#define GC_A2A_TILE_BYTES 32768
+#endif
+#ifndef GC_A2A_UNR
+#define GC_A2A_UNR 4
+#endif
+
+constexpr uint32_t kMaxGrid = GC_SEG_MAX_GRID;
+constexpr uint32_t kA2AMaxGrid = GC_A2A_MAX_GRID;
 
 template <class K, class A>
 gc_status launch(K kernel, const A& args, uint32_t grid, hipStream_t stream) {
@@ -355,13 +369,14 @@ gc_status launch_all_to_all(const A2ACall& c) {
   a.E = c.experts;
   a.d0 = c.d0;
   a.Dg = c.dcount;
-  // About 64 KiB of payload per tile.
-  a.rows_per_tile = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(1u << 20, 65536 / c.row_bytes)));
+  // Fixed payload per tile (GC_A2A_TILE_BYTES, at least one row).
+  a.rows_per_tile = static_cast<uint32_t>(
+      std::max<uint64_t>(1, std::min<uint64_t>(1u << 20, GC_A2A_TILE_BYTES / c.row_bytes)));
   const int64_t ntiles = (total + a.rows_per_tile - 1) / a.rows_per_tile;
-  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(ntiles, kMaxGrid));
+  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(ntiles, kA2AMaxGrid));
   uint64_t m = c.row_bytes;
   for (int s = 0; s < c.nranks; ++s) m |= addr(c.send[s]) | addr(c.recv[s]);
-  if ((m & 15) == 0) return launch(a2a_kernel<u32x4, 4>, a, grid, c.stream);
+  if ((m & 15) == 0) return launch(a2a_kernel<u32x4, GC_A2A_UNR>, a, grid, c.stream);
   if ((m & 3) == 0) return launch(a2a_kernel<uint32_t, 8>, a, grid, c.stream);
   return launch(a2a_kernel<uint8_t, 8>, a, grid, c.stream);
 }

@@ -122,6 +122,22 @@ __device__ __forceinline__ void put(char* p, const Words<Out, VE>& r) {
 
 __device__ __forceinline__ uint32_t next_rank(uint32_t r, uint32_t N) { return r + 1 == N ? 0 : r + 1; }
 
+#ifndef GC_WAVE_CONTIG
+#define GC_WAVE_CONTIG 0
+#endif
+
+// Vector u of this thread within a tile starting at vector tv0.  Default: the
+// workgroup's 256 threads cover 256 consecutive vectors per u.  With
+// GC_WAVE_CONTIG each wavefront covers its U*64 vectors contiguously instead.
+template <int U>
+__device__ __forceinline__ uint64_t tile_vec(uint64_t tv0, int u) {
+#if GC_WAVE_CONTIG
+  return tv0 + (threadIdx.x >> 6) * (64 * U) + u * 64 + (threadIdx.x & 63);
+#else
+  return tv0 + u * kThreads + threadIdx.x;
+#endif
+}
+
 // Element-wise fold of one element E in the chunk's order.
 template <class In, int P>
 __device__ __forceinline__ typename In::Acc fold_one(const RedArgs<P>& a, uint32_t first, uint32_t N, uint64_t E) {
@@ -199,13 +215,13 @@ __device__ __forceinline__ void fold_rest(const RedArgs<P>& a, uint32_t& r, uint
 // skip their stores.
 template <int KIND, class In, class Out, int NF, int U, bool GUARD, int P>
 __device__ __forceinline__ void reduce_tile(const RedArgs<P>& a, uint32_t N, uint32_t j, uint32_t first,
-                                            const ChunkGeom& g, uint64_t vb) {
+                                            const ChunkGeom& g, uint64_t tv0) {
   constexpr int VE = In::VE;
   typedef typename In::Acc Acc;
   uint64_t off[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint64_t v = GUARD ? min(vb + u * kThreads, g.vhi - 1) : vb + u * kThreads;
+    const uint64_t v = GUARD ? min(tile_vec<U>(tv0, u), g.vhi - 1) : tile_vec<U>(tv0, u);
     off[u] = (a.phase + v * VE) * In::ES;
   }
   Acc acc[U][VE];
@@ -223,7 +239,7 @@ __device__ __forceinline__ void reduce_tile(const RedArgs<P>& a, uint32_t N, uin
   const bool avg = a.avg != 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint64_t v = vb + u * kThreads;
+    const uint64_t v = tile_vec<U>(tv0, u);
     Acc o[VE];
 #pragma unroll
     for (int l = 0; l < VE; ++l) o[l] = finish(acc[u][l], avg, a.nf);
@@ -257,11 +273,10 @@ __global__ void __launch_bounds__(kThreads) reduce_vec_kernel(const RedArgs<P> a
     const ChunkGeom g = chunk_geom<VE>(a, j);
     const uint32_t first = a.ring ? next_rank(j, N) : 0;
     const uint64_t tv0 = g.vlo + static_cast<uint64_t>(t) * TV;
-    const uint64_t vb = tv0 + threadIdx.x;
     if (tv0 + TV <= g.vhi) {
-      reduce_tile<KIND, In, Out, NF, U, false>(a, N, j, first, g, vb);
+      reduce_tile<KIND, In, Out, NF, U, false>(a, N, j, first, g, tv0);
     } else if (tv0 < g.vhi) {
-      reduce_tile<KIND, In, Out, NF, U, true>(a, N, j, first, g, vb);
+      reduce_tile<KIND, In, Out, NF, U, true>(a, N, j, first, g, tv0);
     }
 
     if (t == 0) {
@@ -490,6 +505,8 @@ gc_status dispatch_reduce(const gci::ReduceCall& c, const Plan& pl) {
 }
 
 constexpr int kU = GC_RED_U;
+// Below this many tiles (4 per CU on 256 CUs) launches use one vector per thread.
+constexpr uint64_t kSmallTiles = 1024;
 
 template <int KIND, class In, class Out>
 gc_status run_reduce(const gci::ReduceCall& c) {
@@ -516,6 +533,12 @@ gc_status run_reduce(const gci::ReduceCall& c) {
   }
   const uint32_t phase = vec ? static_cast<uint32_t>(ph) : 0u;
   Plan pl{vec, phase, tiles_per_chunk(c, VE, kThreads * kU, vec, phase)};
+  // Small messages: with too few workgroups to cover every CU several times,
+  // one vector per thread doubles the workgroup count.
+  if (vec && kU > 1 && static_cast<uint64_t>(pl.tpc) * N < kSmallTiles) {
+    pl.tpc = tiles_per_chunk(c, VE, kThreads, vec, phase);
+    return dispatch_reduce<KIND, In, Out, 1>(c, pl);
+  }
   return dispatch_reduce<KIND, In, Out, kU>(c, pl);
 }
 
@@ -543,7 +566,9 @@ gc_status run_gather(const gci::ReduceCall& c) {
     const uint64_t first = ph + vlo * VE;
     if (((addr(c.in[j]) + (first - lo) * ES) & 15) != 0) vec = false;
   }
-  const uint32_t tpc = tiles_per_chunk(c, VE, kThreads * kU, vec, vec ? static_cast<uint32_t>(ph) : 0u);
+  uint32_t tpc = tiles_per_chunk(c, VE, kThreads * kU, vec, vec ? static_cast<uint32_t>(ph) : 0u);
+  const bool small = vec && kU > 1 && static_cast<uint64_t>(tpc) * N < kSmallTiles;
+  if (small) tpc = tiles_per_chunk(c, VE, kThreads, vec, static_cast<uint32_t>(ph));
   const uint32_t ntiles = static_cast<uint32_t>(N) * tpc;
   auto fill = [&](auto& a) {
     a.phase = vec ? static_cast<uint32_t>(ph) : 0u;
@@ -553,11 +578,13 @@ gc_status run_gather(const gci::ReduceCall& c) {
   if (N <= 8) {
     RedArgs<8> a = make_args<8>(c);
     fill(a);
+    if (small) return launch(gather_vec_kernel<ES, 1, 8>, a, ntiles, c.stream);
     return vec ? launch(gather_vec_kernel<ES, kU, 8>, a, ntiles, c.stream)
                : launch(gather_elem_kernel<ES, 8>, a, ntiles, c.stream);
   }
   RedArgs<GC_MAX_RANKS> a = make_args<GC_MAX_RANKS>(c);
   fill(a);
+  if (small) return launch(gather_vec_kernel<ES, 1, GC_MAX_RANKS>, a, ntiles, c.stream);
   return vec ? launch(gather_vec_kernel<ES, kU, GC_MAX_RANKS>, a, ntiles, c.stream)
              : launch(gather_elem_kernel<ES, GC_MAX_RANKS>, a, ntiles, c.stream);
 }

@@ -69,6 +69,21 @@ def test_all_reduce(dtype, op, N, S, order):
             assert_same(from_dev(send[r]), xs[r], dtype, "send modified")
 
 
+@pytest.mark.parametrize("dtype,op,N,S", [("bf16", "avg", 4, 4 * (1 << 20) + 13), ("fp32", "sum", 2, (1 << 21) + 6),
+                                          ("bf16", "avg", 8, 8 * 4096 * 128 + 8 * 4095 + 3)])
+def test_all_reduce_two_vectors_per_thread(dtype, op, N, S):
+    # large enough for the launch to use two 16-byte vectors per thread (the
+    # small-message path uses one), compared element by element with the oracle
+    xs = _gen(dtype, N, S, seed=77)
+    want = C.all_reduce(xs, dtype, op, "ring")[0]
+    send = [to_dev(x, dtype) for x in xs]
+    recv = [empty(S, dtype) for _ in range(N)]
+    gc.gc_all_reduce(send, recv, op=op, order="ring")
+    torch.cuda.synchronize()
+    for r in (0, N - 1):
+        _check(from_dev(recv[r]), want, dtype, f"rank {r}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("N", [2, 8])
 def test_all_reduce_in_place(dtype, N):
@@ -162,6 +177,18 @@ def test_all_gather(dtype, N, count):
     gc.gc_all_gather(send, recv)
     torch.cuda.synchronize()
     for d in range(N):
+        assert_same(from_dev(recv[d]), want[d], dtype, f"rank {d}")
+
+
+def test_all_gather_two_vectors_per_thread():
+    N, count, dtype = 8, 128 * 4096 + 8 * 3, "bf16"
+    shards = _gen(dtype, N, count, seed=21)
+    want = C.all_gather(shards)
+    send = [to_dev(x, dtype) for x in shards]
+    recv = [empty(N * count, dtype) for _ in range(N)]
+    gc.gc_all_gather(send, recv)
+    torch.cuda.synchronize()
+    for d in (0, N - 1):
         assert_same(from_dev(recv[d]), want[d], dtype, f"rank {d}")
 
 
