@@ -13,8 +13,10 @@ Prints one JSON line.  value = algorithmic bytes per step / time per step
 (every input read once, every output written once), in GB/s; roofline.frac
 is the dominant kernel's achieved bandwidth over the 8 TB/s HBM3E peak.
 
-Other workloads (--workload): ar_fp32_n4, ddp_llama7b, fsdp_layer_n64,
-moe_a2a_n8 (the remaining parity configurations, measured the same way).
+Other workloads (--workload): ar_fp32_n4, ddp_llama7b, ddp_llama7b_zero_copy,
+fsdp_layer_n64, moe_a2a_n8 (the remaining parity configurations, measured the
+same way; the zero-copy DDP step all-reduces each bucket in place over the
+gradient tensors instead of packing and unpacking it).
 """
 
 import argparse
@@ -32,6 +34,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "effective HBM GB/s (% of peak) for N=8 × 64 MiB bf16 all-reduce on 1 MI355X"
 KERNEL_SOURCES = ["collective_communication_reduction_amd/csrc/reduce.hip",
                   "collective_communication_reduction_amd/csrc/movement.hip",
+                  "collective_communication_reduction_amd/csrc/bucket.hip",
+                  "collective_communication_reduction_amd/csrc/fold.h",
                   "collective_communication_reduction_amd/csrc/device_common.h"]
 
 
@@ -41,11 +45,12 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ar_bf16_n8",
-                   choices=["ar_bf16_n8", "ar_fp32_n4", "ddp_llama7b", "fsdp_layer_n64", "moe_a2a_n8"])
+                   choices=["ar_bf16_n8", "ar_fp32_n4", "ddp_llama7b", "ddp_llama7b_zero_copy", "fsdp_layer_n64",
+                            "moe_a2a_n8"])
     p.add_argument("--replicas", type=int, default=4)
-    p.add_argument("--layout", default="staggered", choices=["staggered", "separate"],
+    p.add_argument("--layout", default="arena", choices=["arena", "staggered", "separate"],
                    help="placement of the rank buffers in HBM")
-    p.add_argument("--stagger", type=int, default=4096, help="bytes between rank slots (staggered layout)")
+    p.add_argument("--stagger", type=int, default=4096, help="extra bytes between consecutive ranks' memory")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -92,17 +97,38 @@ class Workload:
         self.step(k)
 
 
-def rank_buffers(args, nranks, count, tdt):
-    """Rank buffers in HBM: one slab with a 4 KiB per-rank stagger (default), or separate allocations."""
-    import torch
-    import collective_communication_reduction_amd as gc
-    if args.layout == "separate":
-        return [torch.empty(count, dtype=tdt, device="cuda") for _ in range(nranks)]
-    return gc.gc_rank_buffers(nranks, count, tdt, stagger_bytes=args.stagger)
+class Layout:
+    """Where the N rank buffers of a workload live in HBM.
 
+    arena      (default) each rank owns one region of HBM (RankArena: regions a
+               large power of two apart, 4 KiB stagger); every buffer of rank r
+               is carved from region r, as a real rank's buffers sit in its GPU
+    staggered  one allocation per buffer set, ranks 4 KiB apart (gc_rank_buffers)
+    separate   one torch allocation per rank buffer
+    """
 
-def layout_name(args):
-    return "separate allocations" if args.layout == "separate" else f"one slab, {args.stagger} B stagger per rank"
+    def __init__(self, args, nranks):
+        import collective_communication_reduction_amd as gc
+        self.gc = gc
+        self.kind = args.layout
+        self.nranks = nranks
+        self.stagger = args.stagger
+        self.arena = gc.RankArena(nranks, stagger_bytes=args.stagger) if self.kind == "arena" else None
+
+    def buffers(self, count, tdt):
+        import torch
+        if self.kind == "separate":
+            return [torch.empty(count, dtype=tdt, device="cuda") for _ in range(self.nranks)]
+        if self.kind == "staggered":
+            return self.gc.gc_rank_buffers(self.nranks, count, tdt, stagger_bytes=self.stagger)
+        return self.arena.alloc(count, tdt)
+
+    def name(self):
+        if self.kind == "separate":
+            return "separate allocations"
+        if self.kind == "staggered":
+            return f"one allocation per buffer set, {self.stagger} B per-rank stagger"
+        return f"rank arena: {self.arena.region >> 30} GiB region per rank, {self.stagger} B stagger"
 
 
 def _keyed(seed, r, stream=0):
@@ -124,12 +150,13 @@ class AllReduceWorkload(Workload):
         self.dominant = "reduce_vec_kernel (fused all-reduce)"
         self.dominant_bytes = self.bytes_per_step
         self.sets = []
-        self.layout = layout_name(args)
+        L = Layout(args, nranks)
+        self.layout = L.name()
         # enough replica sets that one rotation touches >= 1 GiB (4x the 256 MB MALL)
         reps = max(args.replicas, -(-(1 << 30) // self.bytes_per_step))
         for rep in range(reps):
-            send = rank_buffers(args, nranks, count, tdt)
-            recv = rank_buffers(args, nranks, count, tdt)
+            send = L.buffers(count, tdt)
+            recv = L.buffers(count, tdt)
             for r, t in enumerate(send):
                 if dtype == "bf16":
                     GD.fill_normal_bf16(t, _keyed(args.seed, r), 1e-3)
@@ -163,9 +190,11 @@ class AllReduceWorkload(Workload):
 
 
 class DdpWorkload(Workload):
-    """Llama-7B gradient set, 8 ranks, 25 MiB buckets: pack -> fused all-reduce (avg) -> unpack per bucket."""
+    """Llama-7B gradient set, 8 ranks, 25 MiB buckets: pack -> fused all-reduce (avg) -> unpack per bucket,
+    or (zero_copy) the bucket all-reduced in place over the gradient tensors, with the sum of squares
+    of the synced gradients accumulated for norm clipping."""
 
-    def __init__(self, args):
+    def __init__(self, args, zero_copy=False):
         import torch
         import collective_communication_reduction_amd as gc
         from gen import device as GD
@@ -179,8 +208,9 @@ class DdpWorkload(Workload):
         self.plan = gc.BucketPlan(numels, "bf16", cfg["cap_bytes"], reverse=True)
         total = sum(numels)
         # one flat allocation per rank; tensor t is a view at its model-order offset
-        self.flat = rank_buffers(args, self.N, total, torch.bfloat16)
-        self.layout = layout_name(args)
+        L = Layout(args, self.N)
+        self.flat = L.buffers(total, torch.bfloat16)
+        self.layout = L.name()
         offs, run = [], 0
         for n in numels:
             offs.append(run)
@@ -188,26 +218,42 @@ class DdpWorkload(Workload):
         for r in range(self.N):
             GD.fill_normal_bf16(self.flat[r], _keyed(args.seed, r), cfg["sigma"])
         self.tensors = [self.flat[r][o:o + n] for r in range(self.N) for o, n in zip(offs, numels)]
+        self.tensor_ptrs = gc.gc_pointers(self.tensors)   # the gradients persist: marshal once
         big = max(self.plan.bucket_numel)
-        self.bufs = [rank_buffers(args, self.N, big, torch.bfloat16) for _ in range(2)]
+        self.bufs = [L.buffers(big, torch.bfloat16) for _ in range(2)] if not zero_copy else []
         self.bucket_bytes = [b * 2 for b in self.plan.bucket_numel]
-        self.bytes_per_step = 6 * self.N * sum(self.bucket_bytes)
-        self.dominant = "reduce_vec_kernel (fused all-reduce of each bucket)"
+        self.zero_copy = zero_copy
+        if zero_copy:
+            self.name = "ddp_llama7b_zero_copy"
+            self.sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+            self.bytes_per_step = 2 * self.N * sum(self.bucket_bytes)
+            self.dominant = "bucket_ar_kernel (zero-copy bucket all-reduce + sum of squares)"
+        else:
+            self.bytes_per_step = 6 * self.N * sum(self.bucket_bytes)
+            self.dominant = "reduce_vec_kernel (fused all-reduce of each bucket)"
         self.dominant_bytes = 2 * self.N * sum(self.bucket_bytes)
         torch.cuda.synchronize()
 
     def step(self, k):
         gc, plan, N = self.gc, self.plan, self.N
+        if self.zero_copy:
+            self.sumsq.zero_()
+            for b in range(plan.nbuckets):
+                plan.all_reduce(b, self.tensor_ptrs, N, op="avg", order="ring", sumsq=self.sumsq)
+            return
         for b in range(plan.nbuckets):
             bufs = self.bufs[b & 1]
             n = plan.bucket_numel[b]
             views = [x[:n] for x in bufs]
-            plan.pack(b, self.tensors, views, N)
+            plan.pack(b, self.tensor_ptrs, views, N)
             gc.gc_all_reduce(views, views, op="avg", order="ring", algo="fused")
-            plan.unpack(b, views, self.tensors, N)
+            plan.unpack(b, views, self.tensor_ptrs, N)
 
     def dominant_launch(self, k):
         plan = self.plan
+        if self.zero_copy:
+            self.step(k)
+            return
         for b in range(plan.nbuckets):
             views = [x[:plan.bucket_numel[b]] for x in self.bufs[b & 1]]
             self.gc.gc_all_reduce(views, views, op="avg", order="ring", algo="fused")
@@ -215,7 +261,7 @@ class DdpWorkload(Workload):
     def config(self):
         return {"workload": self.name, "nranks": self.N, "params": sum(self.numels), "storage": "bf16",
                 "buckets": self.plan.nbuckets, "cap_bytes": 25 * 1024 * 1024, "op": "avg", "order": "ring",
-                "layout": self.layout}
+                "zero_copy": self.zero_copy, "layout": self.layout}
 
     def cpu_sample(self, seed):
         import numpy as np
@@ -237,7 +283,7 @@ class DdpWorkload(Workload):
             flats = [OB.pack(per_rank[r], idx, numels) for r in range(self.N)]
             out = C.all_reduce(flats, "bf16", "avg", "ring")
             return [OB.unpack(out[r], idx, numels) for r in range(self.N)]
-        nbytes = 6 * self.N * sum(numels) * 2
+        nbytes = (2 if self.zero_copy else 6) * self.N * sum(numels) * 2
         return run, nbytes, f"oracle pack + ring all-reduce + unpack of bucket {b} truncated to {sum(numels)} elements"
 
 
@@ -255,11 +301,12 @@ class FsdpWorkload(Workload):
         total = sum(n for _, n in fsdp_layer_tensors())
         self.S = -(-total // self.N) * self.N
         self.rc = self.S // self.N
-        self.grads = rank_buffers(args, self.N, self.S, torch.bfloat16)
-        self.gshards = rank_buffers(args, self.N, self.rc, torch.float32)
-        self.pshards = rank_buffers(args, self.N, self.rc, torch.bfloat16)
-        self.params = rank_buffers(args, self.N, self.S, torch.bfloat16)
-        self.layout = layout_name(args)
+        L = Layout(args, self.N)
+        self.grads = L.buffers(self.S, torch.bfloat16)
+        self.gshards = L.buffers(self.rc, torch.float32)
+        self.pshards = L.buffers(self.rc, torch.bfloat16)
+        self.params = L.buffers(self.S, torch.bfloat16)
+        self.layout = L.name()
         for r in range(self.N):
             GD.fill_normal_bf16(self.grads[r], _keyed(args.seed, r, 0), 1e-3)
             GD.fill_normal_bf16(self.pshards[r], _keyed(args.seed, r, 1), 0.02)
@@ -310,13 +357,16 @@ class MoeWorkload(Workload):
         self.splits, rows = moe_send_layout(args.seed, self.N, cfg["tokens"], cfg["experts"], cfg["topk"],
                                             cfg["zipf_s"])
         self.row_bytes = self.H * 2
-        self.send = []
-        for s in range(self.N):
-            t = torch.empty(len(rows[s]) * self.H, dtype=torch.bfloat16, device="cuda")
-            GD.fill_normal_bf16_rows(t, torch.from_numpy(rows[s]).cuda(), self.H, _keyed(args.seed, s), 1.0)
-            self.send.append(t)
+        L = Layout(args, self.N)
+        self.layout = L.name()
         recv_rows = self.splits.sum(axis=(0, 2))
-        self.recv = [torch.empty(int(n) * self.H, dtype=torch.bfloat16, device="cuda") for n in recv_rows]
+        # every rank's buffer sized for the largest rank, at the same offset of each rank's memory
+        send_full = L.buffers(max(len(r) for r in rows) * self.H, torch.bfloat16)
+        recv_full = L.buffers(int(recv_rows.max()) * self.H, torch.bfloat16)
+        self.send = [send_full[s][:len(rows[s]) * self.H] for s in range(self.N)]
+        self.recv = [recv_full[d][:int(recv_rows[d]) * self.H] for d in range(self.N)]
+        for s in range(self.N):
+            GD.fill_normal_bf16_rows(self.send[s], torch.from_numpy(rows[s]).cuda(), self.H, _keyed(args.seed, s), 1.0)
         total_rows = int(self.splits.sum())
         self.bytes_per_step = 2 * total_rows * self.row_bytes
         self.dominant = "a2a_kernel"
@@ -330,7 +380,8 @@ class MoeWorkload(Workload):
 
     def config(self):
         return {"workload": self.name, "nranks": self.N, "tokens": 16384, "hidden": self.H, "experts": 64,
-                "topk": 2, "zipf_s": 1.1, "rows": int(self.splits.sum()), "frac_rows_to_rank0": round(self.frac_dst0, 4)}
+                "topk": 2, "zipf_s": 1.1, "rows": int(self.splits.sum()), "frac_rows_to_rank0": round(self.frac_dst0, 4),
+                "layout": self.layout}
 
     def cpu_sample(self, seed):
         import numpy as np
@@ -362,6 +413,8 @@ def make(args):
         return AllReduceWorkload(args, c["nranks"], c["count"], c["dtype"], c["op"])
     if args.workload == "ddp_llama7b":
         return DdpWorkload(args)
+    if args.workload == "ddp_llama7b_zero_copy":
+        return DdpWorkload(args, zero_copy=True)
     if args.workload == "fsdp_layer_n64":
         return FsdpWorkload(args)
     return MoeWorkload(args)

@@ -11,9 +11,12 @@ importing this package fails if the library has not been built
 The functions carry the C names:
   gc_all_reduce, gc_reduce_scatter, gc_all_gather, gc_all_to_all,
   gc_all_reduce_scratch_bytes, gc_bucket_plan_create / _query / _destroy,
-  gc_bucket_pack, gc_bucket_unpack, gc_status_string, gc_version
-plus BucketPlan, a small owner of a gc_bucket_plan handle, and gc_rank_buffers,
-which lays N rank buffers out in HBM with a per-rank stagger.
+  gc_bucket_pack, gc_bucket_unpack, gc_bucket_all_reduce, gc_status_string,
+  gc_version, gc_last_hip_error
+plus BucketPlan, a small owner of a gc_bucket_plan handle; RankArena, which
+gives each rank its own region of HBM; gc_rank_buffers, which lays N rank
+buffers out in one allocation with a per-rank stagger; and gc_pointers, which
+marshals a pointer array once for buffers synchronised every step.
 """
 
 import ctypes
@@ -74,6 +77,7 @@ _c_plan_query = _sig("gc_bucket_plan_query", _int, _vp, ctypes.POINTER(_int), ct
                      ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_size_t))
 _c_pack = _sig("gc_bucket_pack", _int, _vp, _int, _VPP, _VPP, _int, _vp)
 _c_unpack = _sig("gc_bucket_unpack", _int, _vp, _int, _VPP, _VPP, _int, _vp)
+_c_bucket_ar = _sig("gc_bucket_all_reduce", _int, _vp, _int, _VPP, _int, _int, _int, _vp, _vp)
 _c_plan_destroy = _sig("gc_bucket_plan_destroy", None, _vp)
 _c_status = _sig("gc_status_string", ctypes.c_char_p, _int)
 _c_version = _sig("gc_version", _int)
@@ -119,6 +123,8 @@ def _addr(x):
 def _ptr_array(xs):
     if xs is None:
         return None
+    if isinstance(xs, ctypes.Array):     # already marshalled (gc_pointers)
+        return xs
     arr = (ctypes.c_void_p * max(1, len(xs)))()
     for i, x in enumerate(xs):
         arr[i] = _addr(x)
@@ -138,6 +144,15 @@ def _enum(table, x):
     return table[x] if isinstance(x, str) else int(x)
 
 
+def gc_pointers(tensors):
+    """Marshal a list of tensors (or addresses, or None) into a pointer array once.
+
+    Every call that takes a list also accepts the returned array, which saves
+    rebuilding it when the same buffers are synchronised every step (DDP's
+    gradient tensors persist across steps)."""
+    return _ptr_array(list(tensors))
+
+
 def _stream(stream, like=None):
     """HIP stream handle: an explicit int / torch stream, else torch's current stream on like's device."""
     if stream is None:
@@ -152,7 +167,13 @@ def _stream(stream, like=None):
 
 
 def _first(xs):
-    return xs[0] if xs else None
+    """First tensor-like element (its device picks the stream), or None."""
+    if xs is None or isinstance(xs, ctypes.Array):
+        return None
+    for x in xs:
+        if x is not None and not isinstance(x, int):
+            return x
+    return None
 
 
 def _numel(xs, count):
@@ -245,6 +266,56 @@ def gc_rank_buffers(nranks, count, dtype, device="cuda", stagger_bytes=4096, slo
     return [slab[r * step // es: r * step // es + count] for r in range(nranks)]
 
 
+class RankArena:
+    """Per-rank HBM regions for N ranks on one GPU: every rank owns one region,
+    as a real rank owns its GPU's memory, and all of a rank's buffers are
+    bump-allocated inside it at the same offset on every rank.
+
+    The regions are carved from one allocation; rank r's region starts at
+    r * (region_bytes + stagger_bytes).  A collective reads and writes the same
+    offset on all N ranks at once; regions a large power of two apart plus a
+    small stagger spread those N streams over HBM's channels and stacks.  On
+    MI355X, 16 GiB regions raised the 8 x 64 MiB bf16 all-reduce from about 5.8
+    to 6.2 TB/s, and 4 GiB regions the 64-rank all-gather from about 5.4 to 6.7
+    TB/s.
+
+    region_bytes=None picks the largest power of two up to 16 GiB for which
+    all N regions fit in free device memory (keeping reserve_bytes free), and at
+    least min_bytes.
+    """
+
+    def __init__(self, nranks, region_bytes=None, stagger_bytes=4096, min_bytes=0, device="cuda",
+                 reserve_bytes=4 << 30, max_region=16 << 30):
+        import torch
+        self.nranks = int(nranks)
+        self.stagger = int(stagger_bytes)
+        if region_bytes is None:
+            free = torch.cuda.mem_get_info(torch.device(device))[0] if str(device).startswith("cuda") else 1 << 40
+            region_bytes = 1 << 21
+            while (region_bytes * 2 <= max_region and
+                   self.nranks * (region_bytes * 2 + self.stagger) <= free - reserve_bytes):
+                region_bytes *= 2
+            while region_bytes < min_bytes:
+                region_bytes *= 2
+        self.region = int(region_bytes)
+        self.step = self.region + self.stagger
+        self.slab = torch.empty(self.nranks * self.step, dtype=torch.uint8, device=device)
+        self.used = 0
+
+    def alloc(self, count, dtype):
+        """One buffer of `count` elements per rank, at the same offset of every region."""
+        import torch
+        tdt = {"bf16": torch.bfloat16, "fp32": torch.float32, "int32": torch.int32}.get(dtype, dtype)
+        es = torch.empty((), dtype=tdt).element_size()
+        nbytes = int(count) * es
+        if self.used + nbytes > self.region:
+            raise MemoryError(f"rank region of {self.region} bytes is full")
+        out = [self.slab[r * self.step + self.used: r * self.step + self.used + nbytes].view(tdt)
+               for r in range(self.nranks)]
+        self.used += -(-nbytes // 256) * 256
+        return out
+
+
 # ------------------------------------------------------------------ bucket plan
 
 def gc_bucket_plan_create(numels, dtype, cap_bytes, reverse=True, pad_to=1):
@@ -281,6 +352,14 @@ def gc_bucket_unpack(plan, bucket, bucket_bufs, tensors, nranks, stream=None):
                      _stream(stream, _first(bucket_bufs))), "gc_bucket_unpack")
 
 
+def gc_bucket_all_reduce(plan, bucket, tensors, nranks, op="avg", order="ring", sumsq=None, stream=None):
+    """Zero-copy all-reduce of one bucket, in place over the tensors (rank-major flat list).
+    sumsq: optional CUDA float64 tensor (one element) that receives += sum of squared results."""
+    _check(_c_bucket_ar(plan, int(bucket), _ptr_array(tensors), int(nranks), _enum(_OP, op), _enum(_ORDER, order),
+                        _addr(sumsq), _stream(stream, _first(tensors))),
+           "gc_bucket_all_reduce")
+
+
 class BucketPlan:
     """Owns a gc_bucket_plan handle and caches its query results."""
 
@@ -300,6 +379,9 @@ class BucketPlan:
 
     def unpack(self, bucket, bucket_bufs, tensors, nranks, stream=None):
         gc_bucket_unpack(self.handle, bucket, bucket_bufs, tensors, nranks, stream)
+
+    def all_reduce(self, bucket, tensors, nranks, op="avg", order="ring", sumsq=None, stream=None):
+        gc_bucket_all_reduce(self.handle, bucket, tensors, nranks, op, order, sumsq, stream)
 
     def close(self):
         if self.handle:

@@ -393,6 +393,55 @@ gc_status bucket_segments(const gc_bucket_plan* p, int bucket, const void* const
 
 }  // namespace
 
+extern "C" gc_status gc_bucket_all_reduce(const gc_bucket_plan* p, int bucket, void* const* tensors, int nranks,
+                                          gc_op op, gc_order order, double* sumsq, hipStream_t stream) {
+  GC_TRY(check_ranks(nranks));
+  if (!p || !tensors || bucket < 0 || bucket >= static_cast<int>(p->buckets.size()) || !valid_op(op) ||
+      !valid_order(order))
+    return GC_ERR_INVALID_ARG;
+  if (p->t == GC_INT32 && (op == GC_AVG || sumsq)) return GC_ERR_UNSUPPORTED;
+  if (sumsq && addr(sumsq) % 8) return GC_ERR_INVALID_ARG;
+  const size_t T = p->numel.size();
+  const size_t es = p->es;
+  const std::vector<int>& b = p->buckets[bucket];
+  const uint64_t count = p->padded[bucket];
+  const uint64_t c = chunk_len(count, nranks);
+
+  std::vector<Span> spans;
+  std::vector<void*> slot_ptrs;
+  std::vector<gci::BucketPiece> pieces;
+  uint32_t slot = 0;
+  for (int ti : b) {
+    const uint64_t n = p->numel[ti];
+    if (!n) continue;
+    for (int r = 0; r < nranks; ++r) {
+      void* tp = tensors[static_cast<size_t>(r) * T + ti];
+      if (!tp || addr(tp) % es) return GC_ERR_INVALID_ARG;
+      spans.push_back(span(tp, n * es));
+      slot_ptrs.push_back(tp);
+    }
+    // the tensor's packed range [o, o + n) cut at owner-chunk boundaries
+    const uint64_t o = p->tensor_offset[ti];
+    for (uint64_t lo = o; lo < o + n;) {
+      const uint64_t j = lo / c;
+      const uint64_t hi = std::min(o + n, (j + 1) * c);
+      const uint32_t first = order == GC_ORDER_RING ? static_cast<uint32_t>((j + 1) % nranks) : 0u;
+      pieces.push_back(gci::BucketPiece{lo - o, hi - lo, slot, first});
+      lo = hi;
+    }
+    ++slot;
+  }
+  if (any_overlap(spans)) return GC_ERR_INVALID_ARG;
+  if (sumsq) {
+    const Span sq = span(sumsq, sizeof(double));
+    for (const Span& t : spans)
+      if (overlaps(sq, t)) return GC_ERR_INVALID_ARG;
+  }
+  gci::BucketCall call{slot_ptrs.data(), static_cast<int>(slot), nranks, pieces.data(),
+                       static_cast<int>(pieces.size()), p->t, op == GC_AVG, sumsq, stream};
+  return gci::launch_bucket_all_reduce(call);
+}
+
 extern "C" gc_status gc_bucket_pack(const gc_bucket_plan* p, int bucket, const void* const* tensors,
                                     void* const* bucket_bufs, int nranks, hipStream_t stream) {
   if (!tensors || !bucket_bufs) return GC_ERR_INVALID_ARG;

@@ -1,0 +1,157 @@
+// Device helpers shared by the reduction kernels: unpack a 16-byte vector
+// into reduction-type values, fold N ranks' vectors in a given rank order
+// (all loads of a batch issued before the first add), and pack / store the
+// results in the output type.
+#pragma once
+
+#include "device_common.h"
+
+namespace gcdev {
+
+template <class In>
+__device__ __forceinline__ void unpack(const u32x4& v, typename In::Acc (&x)[In::VE]);
+
+template <>
+__device__ __forceinline__ void unpack<InBf16>(const u32x4& v, float (&x)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(v[k] << 16);
+    x[2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack<InF32>(const u32x4& v, float (&x)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(v[k]);
+}
+template <>
+__device__ __forceinline__ void unpack<InI32>(const u32x4& v, uint32_t (&x)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) x[k] = v[k];
+}
+
+// Packed result words of VE elements of the output type.
+template <class Out, int VE>
+struct Words {
+  static constexpr int NW = VE * Out::ES / 4;
+  uint32_t w[NW];
+};
+
+template <class Out, int VE, class Acc>
+__device__ __forceinline__ Words<Out, VE> pack(const Acc (&x)[VE]) {
+  Words<Out, VE> r;
+  if constexpr (Out::ES == 2) {
+#pragma unroll
+    for (int k = 0; k < VE / 2; ++k) r.w[k] = bf16_bits(x[2 * k]) | (bf16_bits(x[2 * k + 1]) << 16);
+  } else if constexpr (sizeof(Acc) == 4 && __is_same(Acc, float)) {
+#pragma unroll
+    for (int k = 0; k < VE; ++k) r.w[k] = __float_as_uint(x[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < VE; ++k) r.w[k] = x[k];
+  }
+  return r;
+}
+
+template <class Out, int VE>
+__device__ __forceinline__ void put(char* p, const Words<Out, VE>& r) {
+  constexpr int NW = Words<Out, VE>::NW;
+  if constexpr (NW == 2) {
+    st8(p, u32x2{r.w[0], r.w[1]});
+  } else {
+#pragma unroll
+    for (int h = 0; h < NW / 4; ++h) st16(p + 16 * h, u32x4{r.w[4 * h], r.w[4 * h + 1], r.w[4 * h + 2], r.w[4 * h + 3]});
+  }
+}
+
+__device__ __forceinline__ uint32_t next_rank(uint32_t r, uint32_t N) { return r + 1 == N ? 0 : r + 1; }
+
+// `in` points at the N rank pointers (kernel arguments; wavefront-uniform).
+template <class In>
+__device__ __forceinline__ typename In::Acc fold_one(const char* const* in, uint32_t first, uint32_t N, uint64_t E) {
+  typename In::Acc acc = In::one(in[first], E);
+  uint32_t r = first;
+  for (uint32_t k = 1; k < N; ++k) {
+    r = next_rank(r, N);
+    acc = acc + In::one(in[r], E);
+  }
+  return acc;
+}
+
+template <class Out, class Acc>
+__device__ __forceinline__ void put_one(char* base, uint64_t e, Acc x) {
+  if constexpr (Out::ES == 2) {
+    reinterpret_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(bf16_bits(x));
+  } else {
+    reinterpret_cast<Acc*>(base)[e] = x;
+  }
+}
+
+// Loads KB ranks' vectors (ranks r, r+1, ... mod N) for the U byte offsets,
+// all issued before the first add, then folds them into acc in that order.
+// FIRST: the batch starts the fold (acc takes the first rank's values).
+template <class In, int KB, int U, bool FIRST>
+__device__ __forceinline__ void fold_batch(const char* const* in, uint32_t& r, uint32_t N, const uint64_t (&off)[U],
+                                           typename In::Acc (&acc)[U][In::VE]) {
+  constexpr int VE = In::VE;
+  typedef typename In::Acc Acc;
+  u32x4 raw[KB][U];
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    const char* base = in[r];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[k][u] = ld16(base + off[u]);
+    r = next_rank(r, N);
+  }
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Acc x[VE];
+      unpack<In>(raw[k][u], x);
+      if (FIRST && k == 0) {
+#pragma unroll
+        for (int l = 0; l < VE; ++l) acc[u][l] = x[l];
+      } else {
+#pragma unroll
+        for (int l = 0; l < VE; ++l) acc[u][l] = acc[u][l] + x[l];
+      }
+    }
+  }
+}
+
+// The remaining n (1..7) ranks of a runtime-N fold, as one batch.
+template <class In, int U, bool FIRST>
+__device__ __forceinline__ void fold_rest(const char* const* in, uint32_t& r, uint32_t N, uint32_t n,
+                                          const uint64_t (&off)[U], typename In::Acc (&acc)[U][In::VE]) {
+  switch (n) {
+    case 1: fold_batch<In, 1, U, FIRST>(in, r, N, off, acc); break;
+    case 2: fold_batch<In, 2, U, FIRST>(in, r, N, off, acc); break;
+    case 3: fold_batch<In, 3, U, FIRST>(in, r, N, off, acc); break;
+    case 4: fold_batch<In, 4, U, FIRST>(in, r, N, off, acc); break;
+    case 5: fold_batch<In, 5, U, FIRST>(in, r, N, off, acc); break;
+    case 6: fold_batch<In, 6, U, FIRST>(in, r, N, off, acc); break;
+    case 7: fold_batch<In, 7, U, FIRST>(in, r, N, off, acc); break;
+    default: break;
+  }
+}
+
+// Full fold of U vectors at byte offsets `off` over the N ranks in order
+// first, first+1, ... (mod N).  NF > 0: N fixed at compile time.
+template <class In, int NF, int U>
+__device__ __forceinline__ void fold_vec(const char* const* in, uint32_t first, uint32_t N, const uint64_t (&off)[U],
+                                         typename In::Acc (&acc)[U][In::VE]) {
+  uint32_t r = first;
+  if constexpr (NF > 0) {
+    fold_batch<In, NF, U, true>(in, r, NF, off, acc);
+  } else if (N >= 8) {
+    fold_batch<In, 8, U, true>(in, r, N, off, acc);
+    uint32_t k0 = 8;
+    for (; k0 + 8 <= N; k0 += 8) fold_batch<In, 8, U, false>(in, r, N, off, acc);
+    fold_rest<In, U, false>(in, r, N, N - k0, off, acc);
+  } else {
+    fold_rest<In, U, true>(in, r, N, N, off, acc);
+  }
+}
+
+}  // namespace gcdev

@@ -40,6 +40,30 @@ gc_status launch_all_reduce(const ReduceCall& call);
 gc_status launch_reduce_scatter(const ReduceCall& call);
 gc_status launch_all_gather(const ReduceCall& call);
 
+// Zero-copy bucket all-reduce.  A piece is the part of one tensor that falls
+// inside one owner chunk of the bucket's packed index space: elements
+// [lo, lo + len) of the tensor in `slot`, folded starting at rank `first`.
+struct BucketPiece {
+  uint64_t lo;
+  uint64_t len;
+  uint32_t slot;
+  uint32_t first;
+};
+
+struct BucketCall {
+  void* const* slot_ptrs;  // [nslots * nranks], slot-major: rank r's tensor of slot s at [s * nranks + r]
+  int nslots;
+  int nranks;
+  const BucketPiece* pieces;  // ordered by slot
+  int npieces;
+  gc_dtype t;
+  bool avg;
+  double* sumsq;  // device accumulator for the sum of squared results, or nullptr
+  hipStream_t stream;
+};
+
+gc_status launch_bucket_all_reduce(const BucketCall& call);
+
 // One contiguous copy; src == nullptr writes zeros.
 struct Segment {
   const void* src;

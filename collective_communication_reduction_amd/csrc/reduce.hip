@@ -24,6 +24,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "fold.h"
 #include "gc_internal.h"
 
 namespace {
@@ -64,64 +65,6 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const RedArgs<P>& a, uint32_t j)
   return g;
 }
 
-template <class In>
-__device__ __forceinline__ void unpack(const u32x4& v, typename In::Acc (&x)[In::VE]);
-
-template <>
-__device__ __forceinline__ void unpack<InBf16>(const u32x4& v, float (&x)[8]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[2 * k] = __uint_as_float(v[k] << 16);
-    x[2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void unpack<InF32>(const u32x4& v, float (&x)[4]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(v[k]);
-}
-template <>
-__device__ __forceinline__ void unpack<InI32>(const u32x4& v, uint32_t (&x)[4]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) x[k] = v[k];
-}
-
-// Packed result words of VE elements of the output type.
-template <class Out, int VE>
-struct Words {
-  static constexpr int NW = VE * Out::ES / 4;
-  uint32_t w[NW];
-};
-
-template <class Out, int VE, class Acc>
-__device__ __forceinline__ Words<Out, VE> pack(const Acc (&x)[VE]) {
-  Words<Out, VE> r;
-  if constexpr (Out::ES == 2) {
-#pragma unroll
-    for (int k = 0; k < VE / 2; ++k) r.w[k] = bf16_bits(x[2 * k]) | (bf16_bits(x[2 * k + 1]) << 16);
-  } else if constexpr (sizeof(Acc) == 4 && __is_same(Acc, float)) {
-#pragma unroll
-    for (int k = 0; k < VE; ++k) r.w[k] = __float_as_uint(x[k]);
-  } else {
-#pragma unroll
-    for (int k = 0; k < VE; ++k) r.w[k] = x[k];
-  }
-  return r;
-}
-
-template <class Out, int VE>
-__device__ __forceinline__ void put(char* p, const Words<Out, VE>& r) {
-  constexpr int NW = Words<Out, VE>::NW;
-  if constexpr (NW == 2) {
-    st8(p, u32x2{r.w[0], r.w[1]});
-  } else {
-#pragma unroll
-    for (int h = 0; h < NW / 4; ++h) st16(p + 16 * h, u32x4{r.w[4 * h], r.w[4 * h + 1], r.w[4 * h + 2], r.w[4 * h + 3]});
-  }
-}
-
-__device__ __forceinline__ uint32_t next_rank(uint32_t r, uint32_t N) { return r + 1 == N ? 0 : r + 1; }
-
 #ifndef GC_WAVE_CONTIG
 #define GC_WAVE_CONTIG 0
 #endif
@@ -139,75 +82,6 @@ __device__ __forceinline__ uint64_t tile_vec(uint64_t tv0, int u) {
 }
 
 // Element-wise fold of one element E in the chunk's order.
-template <class In, int P>
-__device__ __forceinline__ typename In::Acc fold_one(const RedArgs<P>& a, uint32_t first, uint32_t N, uint64_t E) {
-  typename In::Acc acc = In::one(a.in[first], E);
-  uint32_t r = first;
-  for (uint32_t k = 1; k < N; ++k) {
-    r = next_rank(r, N);
-    acc = acc + In::one(a.in[r], E);
-  }
-  return acc;
-}
-
-template <class Out, class Acc>
-__device__ __forceinline__ void put_one(char* base, uint64_t e, Acc x) {
-  if constexpr (Out::ES == 2) {
-    reinterpret_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(bf16_bits(x));
-  } else {
-    reinterpret_cast<Acc*>(base)[e] = x;
-  }
-}
-
-// Loads KB ranks' vectors (ranks r, r+1, ... mod N) for the U byte offsets,
-// all issued before the first add, then folds them into acc in that order.
-// FIRST: the batch starts the fold (acc takes the first rank's values).
-template <class In, int KB, int U, bool FIRST, int P>
-__device__ __forceinline__ void fold_batch(const RedArgs<P>& a, uint32_t& r, uint32_t N, const uint64_t (&off)[U],
-                                           typename In::Acc (&acc)[U][In::VE]) {
-  constexpr int VE = In::VE;
-  typedef typename In::Acc Acc;
-  u32x4 raw[KB][U];
-#pragma unroll
-  for (int k = 0; k < KB; ++k) {
-    const char* base = a.in[r];
-#pragma unroll
-    for (int u = 0; u < U; ++u) raw[k][u] = ld16(base + off[u]);
-    r = next_rank(r, N);
-  }
-#pragma unroll
-  for (int k = 0; k < KB; ++k) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      Acc x[VE];
-      unpack<In>(raw[k][u], x);
-      if (FIRST && k == 0) {
-#pragma unroll
-        for (int l = 0; l < VE; ++l) acc[u][l] = x[l];
-      } else {
-#pragma unroll
-        for (int l = 0; l < VE; ++l) acc[u][l] = acc[u][l] + x[l];
-      }
-    }
-  }
-}
-
-// The remaining n (1..7) ranks of a runtime-N fold, as one batch.
-template <class In, int U, bool FIRST, int P>
-__device__ __forceinline__ void fold_rest(const RedArgs<P>& a, uint32_t& r, uint32_t N, uint32_t n,
-                                          const uint64_t (&off)[U], typename In::Acc (&acc)[U][In::VE]) {
-  switch (n) {
-    case 1: fold_batch<In, 1, U, FIRST>(a, r, N, off, acc); break;
-    case 2: fold_batch<In, 2, U, FIRST>(a, r, N, off, acc); break;
-    case 3: fold_batch<In, 3, U, FIRST>(a, r, N, off, acc); break;
-    case 4: fold_batch<In, 4, U, FIRST>(a, r, N, off, acc); break;
-    case 5: fold_batch<In, 5, U, FIRST>(a, r, N, off, acc); break;
-    case 6: fold_batch<In, 6, U, FIRST>(a, r, N, off, acc); break;
-    case 7: fold_batch<In, 7, U, FIRST>(a, r, N, off, acc); break;
-    default: break;
-  }
-}
-
 // One tile of U vectors per thread: fold, epilogue, store.  GUARD is false for
 // tiles that lie wholly inside the chunk (no predicates anywhere, so the
 // compiler keeps every load of a batch in flight together); the chunk's last,
@@ -225,17 +99,7 @@ __device__ __forceinline__ void reduce_tile(const RedArgs<P>& a, uint32_t N, uin
     off[u] = (a.phase + v * VE) * In::ES;
   }
   Acc acc[U][VE];
-  uint32_t r = first;
-  if constexpr (NF > 0) {
-    fold_batch<In, NF, U, true>(a, r, NF, off, acc);
-  } else if (N >= 8) {
-    fold_batch<In, 8, U, true>(a, r, N, off, acc);
-    uint32_t k0 = 8;
-    for (; k0 + 8 <= N; k0 += 8) fold_batch<In, 8, U, false>(a, r, N, off, acc);
-    fold_rest<In, U, false>(a, r, N, N - k0, off, acc);
-  } else {
-    fold_rest<In, U, true>(a, r, N, N, off, acc);
-  }
+  fold_vec<In, NF, U>(a.in, first, N, off, acc);
   const bool avg = a.avg != 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -288,7 +152,7 @@ __global__ void __launch_bounds__(kThreads) reduce_vec_kernel(const RedArgs<P> a
       const uint64_t nscalar = nhead + (g.hi - tail_beg);
       if (threadIdx.x < nscalar) {
         const uint64_t E = threadIdx.x < nhead ? g.lo + threadIdx.x : tail_beg + (threadIdx.x - nhead);
-        const Acc x = finish(fold_one<In>(a, first, N, E), avg, a.nf);
+        const Acc x = finish(fold_one<In>(a.in, first, N, E), avg, a.nf);
         if constexpr (KIND == kAllReduce) {
           for (uint32_t q = 0; q < N; ++q) put_one<Out>(a.out[q], E, x);
         } else {
@@ -315,7 +179,7 @@ __global__ void __launch_bounds__(kThreads) reduce_elem_kernel(const RedArgs<P> 
     for (int u = 0; u < 4; ++u) {
       const uint64_t E = lo + static_cast<uint64_t>(t) * TE + u * kThreads + threadIdx.x;
       if (E < hi) {
-        const typename In::Acc x = finish(fold_one<In>(a, first, N, E), avg, a.nf);
+        const typename In::Acc x = finish(fold_one<In>(a.in, first, N, E), avg, a.nf);
         if constexpr (KIND == kAllReduce) {
           for (uint32_t r = 0; r < N; ++r) put_one<Out>(a.out[r], E, x);
         } else {

@@ -173,6 +173,29 @@ gc_status gc_bucket_pack(const gc_bucket_plan* plan, int bucket, const void* con
 gc_status gc_bucket_unpack(const gc_bucket_plan* plan, int bucket, const void* const* bucket_bufs,
                            void* const* tensors, int nranks, hipStream_t stream);
 
+/*
+ * Zero-copy bucketed all-reduce: DDP with gradient_as_bucket_view (AIG6
+ * §6.2.4), where gradients live in the bucket instead of being copied into it.
+ * All-reduces bucket `bucket` directly over the tensors, in place:
+ * tensors[r*ntensors + t][k] becomes op over ranks i of tensors[i*ntensors + t][k],
+ * for every tensor t of the bucket.  Element k of tensor t sits at
+ * offset_t + k of the packed bucket, whose bucket_numel elements (padding
+ * included) form the owner chunks that fix the fold order, so the result is
+ * bit-identical to gc_bucket_pack, gc_all_reduce over bucket_numel elements
+ * with the same op and order, then gc_bucket_unpack; it moves 2*N*B bytes
+ * instead of 6*N*B.
+ *   tensors  HOST array of nranks*ntensors device pointers (rank-major); only
+ *            the bucket's tensors are read; they must not overlap.
+ *   sumsq    optional DEVICE pointer to one double (NULL: none; floating types
+ *            only).  The sum over the bucket's elements of the squared results,
+ *            as stored (rank 0's copy), is ADDED to *sumsq with device atomics,
+ *            so callers zero it once and accumulate over buckets for gradient-norm
+ *            clipping.  The order of the atomic additions is not fixed: the
+ *            norm's last bits may differ between runs.
+ */
+gc_status gc_bucket_all_reduce(const gc_bucket_plan* plan, int bucket, void* const* tensors, int nranks,
+                               gc_op op, gc_order order, double* sumsq, hipStream_t stream);
+
 void gc_bucket_plan_destroy(gc_bucket_plan* plan);
 
 /* Static, human-readable name of a status code. */

@@ -84,3 +84,29 @@ def uneven_dim0_shards(rows, world_size):
     """
     c = -(-rows // world_size) if rows else 0
     return [(min(rows, i * c), min(rows, (i + 1) * c)) for i in range(world_size)]
+
+
+def bucket_all_reduce(per_rank_tensors, bucket, numels, dtype, op="avg", order="ring", pad_to=1):
+    """Zero-copy bucketed all-reduce, defined as its plain composition: pack the
+    bucket on every rank, all-reduce the packed buffers (padding included), and
+    unpack.  Returns per rank a dict tensor index -> reduced values.
+    (AIG6 §6.2.4: gradient_as_bucket_view makes the bucket the gradients'
+    storage; the reduction itself is the bucket's all-reduce.)"""
+    from .collectives import all_reduce
+    flats = [pack(per_rank_tensors[r], bucket, numels, pad_to) for r in range(len(per_rank_tensors))]
+    reduced = all_reduce(flats, dtype, op, order)
+    return [unpack(reduced[r], bucket, numels) for r in range(len(reduced))]
+
+
+def sum_of_squares(values, dtype):
+    """Exact sum of squared element values (a Fraction), for gradient-norm
+    clipping after the sync (AIG6 §6.8.1: clip_grad_norm_ on the synced gradients).
+    bf16 values are given as bit patterns."""
+    from fractions import Fraction
+    from .numerics import bf16_to_f32
+    v = bf16_to_f32(values) if dtype == "bf16" else np.asarray(values, dtype=np.float32)
+    total = Fraction(0)
+    for x in v.astype(np.float64):
+        f = Fraction(float(x))
+        total += f * f
+    return total

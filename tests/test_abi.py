@@ -168,3 +168,19 @@ def test_rank_buffers_layout():
         assert b.data_ptr() - base == r * ((1 << 20) + 4096)
     with pytest.raises(ValueError):
         gc.gc_rank_buffers(2, 10, "fp32", device="cpu", stagger_bytes=6)
+
+
+def test_bucket_all_reduce_validation():
+    plan = gc.BucketPlan([8, 8], "bf16", 1 << 20)
+    tensors = _ptrs(4)
+    assert _status(gc.gc_bucket_all_reduce, plan.handle, 3, tensors, 2, stream=0) == gc.GC_ERR_INVALID_ARG
+    assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, tensors[:3] + [0], 2, stream=0) == gc.GC_ERR_INVALID_ARG
+    overl = [tensors[0], tensors[0] + 8, tensors[2], tensors[3]]          # rank 0's two tensors overlap
+    assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, overl, 2, stream=0) == gc.GC_ERR_INVALID_ARG
+    assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, tensors, 2, sumsq=FAKE + 4,
+                   stream=0) == gc.GC_ERR_INVALID_ARG                     # misaligned accumulator
+    ip = gc.BucketPlan([8], "int32", 1 << 20)
+    assert _status(gc.gc_bucket_all_reduce, ip.handle, 0, _ptrs(2), 2, op="avg", stream=0) == gc.GC_ERR_UNSUPPORTED
+    assert _status(gc.gc_bucket_all_reduce, ip.handle, 0, _ptrs(2), 2, op="sum", sumsq=FAKE,
+                   stream=0) == gc.GC_ERR_UNSUPPORTED
+    assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, tensors, 65, stream=0) == gc.GC_ERR_UNSUPPORTED

@@ -318,6 +318,77 @@ def test_bucket_pack_unpack(dtype, cap, pad, seed):
                     assert_same(from_dev(outs[r][t]), host[r][t], dtype, f"unpack {t}")
 
 
+@pytest.mark.parametrize("dtype,op,N,pad,seed", [("bf16", "avg", 8, 1, 0), ("bf16", "avg", 3, 8, 1), ("fp32", "sum", 2, 1, 2),
+                                                 ("fp32", "avg", 16, 16, 3), ("int32", "sum", 4, 1, 4),
+                                                 ("bf16", "sum", 1, 1, 5), ("bf16", "avg", 64, 64, 6)])
+@pytest.mark.parametrize("order", ["ring", "rank"])
+def test_bucket_all_reduce_zero_copy(dtype, op, N, pad, seed, order):
+    # in place over the tensors; must equal pack -> all-reduce -> unpack of the oracle bit for bit
+    rng = np.random.default_rng(seed)
+    numels = [int(x) for x in rng.integers(1, 3000, size=7)] + [4096 * 3 + 8, 0, 1, 5]
+    if N == 64:
+        numels = [int(x) for x in rng.integers(1, 600, size=4)]
+    T = len(numels)
+    host = [[_gen(dtype, 1, n, seed=seed * 1000 + r * 37 + t)[0] for t, n in enumerate(numels)] for r in range(N)]
+    cap = 9000 * ELEM[dtype]
+    plan = gc.BucketPlan(numels, dtype, cap, reverse=True, pad_to=pad)
+    want_buckets = OB.assign_buckets(numels, ELEM[dtype], cap, reverse=True)
+    # tensors as views at element offsets inside one allocation per rank (some not 16-byte aligned)
+    flat = [empty(sum(numels) + 8 * T, dtype) for _ in range(N)]
+    offs, run = [], 0
+    for n in numels:
+        offs.append(run)
+        run += n + (3 if dtype == "bf16" else 1)
+    # seed 2: odd ranks shifted by one element, so pieces take the element-wise path
+    shift = [(r % 2) if seed == 2 else 0 for r in range(N)]
+    dev = [[flat[r][shift[r] + offs[t]:shift[r] + offs[t] + numels[t]] for t in range(T)] for r in range(N)]
+    for r in range(N):
+        for t in range(T):
+            if numels[t]:
+                dev[r][t].copy_(to_dev(host[r][t], dtype))
+    flat_list = [dev[r][t] if numels[t] else None for r in range(N) for t in range(T)]
+    sq = torch.zeros(1, dtype=torch.float64, device=DEV)
+    use_sq = dtype != "int32"
+    for b in range(plan.nbuckets):
+        plan.all_reduce(b, flat_list, N, op=op, order=order, sumsq=sq if use_sq else None)
+    torch.cuda.synchronize()
+    exact_sq = 0
+    for b, ts in enumerate(want_buckets):
+        want = OB.bucket_all_reduce(host, ts, numels, dtype, op, order, pad_to=pad)
+        for t in ts:
+            if numels[t]:
+                for r in range(N):
+                    _check(from_dev(dev[r][t]), want[r][t], dtype, f"bucket {b} tensor {t} rank {r}")
+                if use_sq:
+                    exact_sq += OB.sum_of_squares(want[0][t], dtype)
+    if use_sq:
+        got = float(sq.item())
+        assert abs(got - float(exact_sq)) <= 1e-12 * float(exact_sq) + 1e-300
+
+
+def test_bucket_all_reduce_equals_pack_path_on_device():
+    N, dtype = 8, "bf16"
+    numels = [4096 * 5, 4096, 12345, 8, 4096 * 9]
+    T = len(numels)
+    host = [[_gen(dtype, 1, n, seed=r * 10 + t)[0] for t, n in enumerate(numels)] for r in range(N)]
+    a = [[to_dev(host[r][t], dtype) for t in range(T)] for r in range(N)]
+    b = [[to_dev(host[r][t], dtype) for t in range(T)] for r in range(N)]
+    plan = gc.BucketPlan(numels, dtype, 40000 * 2, reverse=True)
+    bufs = [empty(max(plan.bucket_numel), dtype) for _ in range(N)]
+    fa = [a[r][t] for r in range(N) for t in range(T)]
+    fb = [b[r][t] for r in range(N) for t in range(T)]
+    for k in range(plan.nbuckets):
+        plan.all_reduce(k, fa, N)
+        views = [x[:plan.bucket_numel[k]] for x in bufs]
+        plan.pack(k, fb, views, N)
+        gc.gc_all_reduce(views, views, op="avg")
+        plan.unpack(k, views, fb, N)
+    torch.cuda.synchronize()
+    for r in range(N):
+        for t in range(T):
+            assert torch.equal(a[r][t].view(torch.int16), b[r][t].view(torch.int16))
+
+
 def gc_torch(dtype):
     return {"bf16": torch.bfloat16, "fp32": torch.float32, "int32": torch.int32}[dtype]
 

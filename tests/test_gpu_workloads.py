@@ -1,5 +1,6 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration and
-HBM layout bench.py times (rank buffers in one slab, 4 KiB per-rank stagger).
+HBM layout bench.py times (a RankArena: each rank's buffers in its own region
+of HBM, 4 KiB stagger between ranks).
 
 At these sizes the step-by-step oracle cannot hold the inputs, so each test
 checks (a) sampled outputs the oracle computes one by one from inputs it
@@ -56,11 +57,12 @@ def test_ar_fp32_n4_full():
     N, S = cfg["nranks"], cfg["count"]
     xs = [G.uniform_f32(G.stream_key(SEED, r, 0), np.arange(S)) for r in range(N)]
     want = C.all_reduce(xs, "fp32", "sum", "ring")[0]
-    send = gc.gc_rank_buffers(N, S, "fp32")
+    arena = gc.RankArena(N)
+    send = arena.alloc(S, "fp32")
     for r in range(N):
         GD.fill_uniform_f32(send[r], G.stream_key(SEED, r, 0))
     for algo in ("fused", "rs_ag"):
-        recv = gc.gc_rank_buffers(N, S, "fp32")
+        recv = arena.alloc(S, "fp32")
         scratch = torch.empty(gc.gc_all_reduce_scratch_bytes(S, N, "fp32"), dtype=torch.uint8, device=DEV)
         gc.gc_all_reduce(send, recv, op="sum", order="ring", algo=algo, scratch=scratch)
         torch.cuda.synchronize()
@@ -71,14 +73,15 @@ def test_ar_fp32_n4_full():
 def test_ar_bf16_n8_full():
     cfg = WORKLOADS["ar_bf16_n8"]
     N, S, sigma = cfg["nranks"], cfg["count"], cfg["sigma"]
-    send = gc.gc_rank_buffers(N, S, "bf16")
+    arena = gc.RankArena(N)
+    send = arena.alloc(S, "bf16")
     keys = [G.stream_key(SEED, r, 0) for r in range(N)]
     for r in range(N):
         GD.fill_normal_bf16(send[r], keys[r], sigma)
-    recv = gc.gc_rank_buffers(N, S, "bf16")
+    recv = arena.alloc(S, "bf16")
     gc.gc_all_reduce(send, recv, op="avg", order="ring", algo="fused")
     # the same all-reduce as reduce-scatter then all-gather, separately
-    recv2 = gc.gc_rank_buffers(N, S, "bf16")
+    recv2 = arena.alloc(S, "bf16")
     scratch = torch.empty(gc.gc_all_reduce_scratch_bytes(S, N, "bf16"), dtype=torch.uint8, device=DEV)
     gc.gc_all_reduce(send, recv2, op="avg", order="ring", algo="rs_ag", scratch=scratch)
     torch.cuda.synchronize()
@@ -105,12 +108,13 @@ def test_ddp_llama7b_full_step():
     numels, offs = _llama_layout()
     total = int(offs[-1])
     keys = [G.stream_key(SEED, r, 0) for r in range(N)]
-    flat = gc.gc_rank_buffers(N, total, "bf16")
+    arena = gc.RankArena(N, min_bytes=total * 2 + (1 << 30))
+    flat = arena.alloc(total, "bf16")
     for r in range(N):
         GD.fill_normal_bf16(flat[r], keys[r], sigma)
     tensors = [flat[r][int(offs[t]):int(offs[t]) + numels[t]] for r in range(N) for t in range(len(numels))]
     plan = gc.BucketPlan(numels, "bf16", cap, reverse=True)
-    bufs = [gc.gc_rank_buffers(N, max(plan.bucket_numel), "bf16") for _ in range(2)]
+    bufs = [arena.alloc(max(plan.bucket_numel), "bf16") for _ in range(2)]
     for b in range(plan.nbuckets):                      # one step, exactly as bench.py runs it
         views = [x[:plan.bucket_numel[b]] for x in bufs[b & 1]]
         plan.pack(b, tensors, views, N)
@@ -142,6 +146,50 @@ def test_ddp_llama7b_full_step():
     plan.close()
 
 
+def test_ddp_llama7b_zero_copy_full_step():
+    # the bench's zero-copy step: every bucket all-reduced in place over the gradient tensors,
+    # with the sum of squares of the synced gradients accumulated on the device
+    cfg = WORKLOADS["ddp_llama7b"]
+    N, sigma, cap = cfg["nranks"], cfg["sigma"], cfg["cap_bytes"]
+    numels, offs = _llama_layout()
+    total = int(offs[-1])
+    keys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    arena = gc.RankArena(N, min_bytes=total * 2 + (1 << 30))
+    flat = arena.alloc(total, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(flat[r], keys[r], sigma)
+    tensors = [flat[r][int(offs[t]):int(offs[t]) + numels[t]] for r in range(N) for t in range(len(numels))]
+    plan = gc.BucketPlan(numels, "bf16", cap, reverse=True)
+    sq = torch.zeros(1, dtype=torch.float64, device=DEV)
+    for b in range(plan.nbuckets):
+        plan.all_reduce(b, tensors, N, op="avg", order="ring", sumsq=sq)
+    torch.cuda.synchronize()
+    for r in range(1, N):
+        assert torch.equal(flat[r].view(torch.int16), flat[0].view(torch.int16)), f"rank {r} differs"
+    rng = np.random.default_rng(6)
+    oracle_buckets = OB.assign_buckets(numels, 2, cap, reverse=True)
+    flat_pos, want = [], []
+    for b, ts in enumerate(oracle_buckets):
+        boffs, used, _ = OB.bucket_layout(ts, numels)
+        e = np.unique(np.concatenate([rng.integers(0, used, size=48), [0, used - 1],
+                                      [min(used - 1, j * -(-used // N)) for j in range(N)]]))
+        starts = np.asarray(boffs)
+        which = np.searchsorted(starts, e, side="right") - 1
+        fidx = np.array([offs[ts[w]] + (ee - starts[w]) for w, ee in zip(which, e)], dtype=np.int64)
+        vals = np.stack([G.normal_bf16(keys[r], fidx, sigma) for r in range(N)])
+        want.append(SM.all_reduce_at(vals, e, used, "bf16", "avg", "ring"))
+        flat_pos.append(fidx)
+    got = _gather(flat[2], np.concatenate(flat_pos))
+    assert_same(got, np.concatenate(want), "bf16", "sampled zero-copy outputs")
+    # the accumulated sum of squares equals the squared norm of the synced gradients (any order: fp64
+    # relative bound over 6.7e9 terms)
+    norm2 = 0.0
+    for lo in range(0, total, 1 << 28):                     # in pieces: the float64 copy would be 54 GB
+        norm2 += float((flat[0][lo:lo + (1 << 28)].double() ** 2).sum().item())
+    assert abs(float(sq.item()) - norm2) <= 1e-9 * norm2
+    plan.close()
+
+
 def test_fsdp_layer_n64_full():
     N = WORKLOADS["fsdp_layer_n64"]["nranks"]
     numels = [n for _, n in fsdp_layer_tensors()]
@@ -149,10 +197,11 @@ def test_fsdp_layer_n64_full():
     rc = S // N
     gkeys = [G.stream_key(SEED, r, 0) for r in range(N)]
     pkeys = [G.stream_key(SEED, r, 1) for r in range(N)]
-    grads = gc.gc_rank_buffers(N, S, "bf16")
+    arena = gc.RankArena(N)
+    grads = arena.alloc(S, "bf16")
     for r in range(N):
         GD.fill_normal_bf16(grads[r], gkeys[r], 1e-3)
-    gshards = gc.gc_rank_buffers(N, rc, "fp32")
+    gshards = arena.alloc(rc, "fp32")
     gc.gc_reduce_scatter(grads, gshards, op="avg", order="ring")
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
@@ -161,12 +210,10 @@ def test_fsdp_layer_n64_full():
         vals = np.stack([G.normal_bf16(gkeys[i], j * rc + k, 1e-3) for i in range(N)])
         want = SM.reduce_scatter_at(vals, np.full(len(k), j), k, rc, "bf16", "fp32", "avg", "ring")
         assert_same(_gather(gshards[j], k), want, "fp32", f"reduce-scatter owner {j}")
-    del grads, gshards
-    torch.cuda.empty_cache()
-    pshards = gc.gc_rank_buffers(N, rc, "bf16")
+    pshards = arena.alloc(rc, "bf16")
     for r in range(N):
         GD.fill_normal_bf16(pshards[r], pkeys[r], 0.02)
-    params = gc.gc_rank_buffers(N, S, "bf16")
+    params = arena.alloc(S, "bf16")
     gc.gc_all_gather(pshards, params)
     torch.cuda.synchronize()
     for d in range(1, N):
@@ -181,13 +228,14 @@ def test_moe_a2a_n8_full():
     cfg = WORKLOADS["moe_a2a_n8"]
     N, H = cfg["nranks"], cfg["hidden"]
     splits, rows = moe_send_layout(SEED, N, cfg["tokens"], cfg["experts"], cfg["topk"], cfg["zipf_s"])
-    send = []
-    for s in range(N):
-        t = torch.empty(len(rows[s]) * H, dtype=torch.bfloat16, device=DEV)
-        GD.fill_normal_bf16_rows(t, torch.from_numpy(rows[s]).to(DEV), H, G.stream_key(SEED, s, 0), 1.0)
-        send.append(t)
     recv_rows = splits.sum(axis=(0, 2))
-    recv = [torch.empty(int(n) * H, dtype=torch.bfloat16, device=DEV) for n in recv_rows]
+    arena = gc.RankArena(N)
+    send_full = arena.alloc(max(len(r) for r in rows) * H, "bf16")
+    recv_full = arena.alloc(int(recv_rows.max()) * H, "bf16")
+    send = [send_full[s][:len(rows[s]) * H] for s in range(N)]
+    recv = [recv_full[d][:int(recv_rows[d]) * H] for d in range(N)]
+    for s in range(N):
+        GD.fill_normal_bf16_rows(send[s], torch.from_numpy(rows[s]).to(DEV), H, G.stream_key(SEED, s, 0), 1.0)
     gc.gc_all_to_all(send, recv, splits, H * 2)
     torch.cuda.synchronize()
     # the oracle's permutation applied to global row ids gives every received row's source row

@@ -103,3 +103,33 @@ def test_fsdp_layer_flat_size():
     numels = [n for _, n in fsdp_layer_tensors()]
     _, used, padded, shards = B.flat_param_shards(numels, 64)
     assert used == 202_383_360 and padded == used and shards[1] == (3_162_240, 6_324_480)
+
+
+def test_bucket_all_reduce_is_pack_allreduce_unpack():
+    from oracle import collectives as C
+    from oracle.numerics import f32_to_bf16
+    rng = np.random.default_rng(11)
+    N = 3
+    numels = [5, 1, 9, 4]
+    tensors = [[f32_to_bf16(rng.normal(size=n).astype(np.float32)) for n in numels] for _ in range(N)]
+    b = [3, 1, 0]
+    out = B.bucket_all_reduce(tensors, b, numels, "bf16", "avg", "ring", pad_to=4)
+    # written out by hand: the packed bucket is 4 + 1 + 5 = 10 elements padded to 12, chunks of 4
+    flat = [np.concatenate([tensors[r][3], tensors[r][1], tensors[r][0], np.zeros(2, np.uint16)]) for r in range(N)]
+    full = C.all_reduce(flat, "bf16", "avg", "ring")
+    for r in range(N):
+        assert np.array_equal(out[r][3], full[r][0:4])
+        assert np.array_equal(out[r][1], full[r][4:5])
+        assert np.array_equal(out[r][0], full[r][5:10])
+        assert 2 not in out[r]
+
+
+def test_sum_of_squares_closed_forms():
+    from fractions import Fraction
+    from oracle.numerics import f32_to_bf16
+    assert B.sum_of_squares(np.full(10, 3.0, np.float32), "fp32") == 90
+    assert B.sum_of_squares(f32_to_bf16(np.array([0.5, -0.25], np.float32)), "bf16") == Fraction(5, 16)
+    assert B.sum_of_squares(np.zeros(0, np.float32), "fp32") == 0
+    x = np.random.default_rng(0).normal(size=500).astype(np.float32)
+    import math
+    assert abs(float(B.sum_of_squares(x, "fp32")) - math.fsum(float(v) ** 2 for v in x)) < 1e-12
