@@ -67,14 +67,15 @@ def kernel_hash():
 
 
 def traffic_from_profiles(workload):
-    """HBM bytes per launch of the dominant kernel, from the committed counter
-    summary, if it was taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
+    """HBM bytes of the dominant kernel (per launch, or per step for workloads
+    that launch it many times per step), from the committed rocprofv3 summary,
+    if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_profile.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
     m = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", text)
-    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    t = re.search(r"traffic_bytes_per_(?:launch|step):\s*([0-9]+)", text)
     if not m or not t or m.group(1) != kernel_hash():
         return None
     return int(t.group(1))
