@@ -25,7 +25,9 @@ Modules
                emulated step by step with traffic counters, rank-order fold,
                exact brute-force sum, all-to-all(v)
   buckets      DDP bucket assignment, bucket pack / unpack, FlatParameter
-               flatten / pad / shard
+               flatten / pad / shard, zero-copy bucket all-reduce, sum of squares
+  moe          expert-parallel MoE around the all-to-all: routing plan,
+               dispatch from token order, weighted combine back to token order
   sampled      evaluation of single output elements, for checks at sizes the
                step-by-step emulation cannot hold in memory
   cost_model   the pages' alpha-beta estimates (context numbers)
@@ -33,8 +35,9 @@ Modules
 Parity status: every function here is pinned by a CPU test (tests/test_oracle_*)
 against the pages' worked examples, closed forms, library routines or brute
 force, except the points the pages leave open (bucket closing rule, MoE routing
-details); those are readings, recorded as such, and the bucket rule is pinned
-only by the invariants it must satisfy.
+details, the order and rounding of the MoE combine); those are readings,
+recorded as such, pinned by hand-worked examples and the invariants they must
+satisfy.
 """
 
-from . import numerics, collectives, buckets, sampled, cost_model  # noqa: F401
+from . import numerics, collectives, buckets, sampled, cost_model, moe  # noqa: F401
