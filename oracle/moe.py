@@ -18,6 +18,12 @@ them is what this module defines, as compositions of `collectives.all_to_all`:
                pages give none): rows widened to fp32, each product w_k * y_k
                rounded to fp32, the products added in k order starting from
                k = 0, the sum rounded to the row type (bf16: nearest-even).
+
+Dropped routes (a reading: the pages name a capacity limit that drops tokens
+but no format for it): an expert id outside [0, N * E) marks a route that is
+not sent.  It is not counted in the splits, its destination is (-1, -1),
+dispatch copies nothing for it and combine leaves it out of the sum (the fold
+starts at the first route kept); a token with no route kept gets zeros.
 """
 
 import numpy as np
@@ -41,17 +47,18 @@ def route_plan(experts, nranks, experts_per_rank):
         T, K = ex.shape
         g = ex.reshape(-1)
         tok = np.repeat(np.arange(T), K)
+        keep = (g >= 0) & (g < N * E)
         order = np.lexsort((tok, g))          # send order: by global expert, then token
-        orders.append(order)
-        counts = np.bincount(g, minlength=N * E)
+        orders.append(order[keep[order]])
+        counts = np.bincount(g[keep], minlength=N * E)
         splits[s] = counts.reshape(N, E)
     roff = a2a_recv_offsets(splits)
     dest_rank, dest_row = [], []
     for s in range(N):
         ex = np.asarray(experts[s], dtype=np.int64)
         g = ex.reshape(-1)
-        dr = np.empty(len(g), dtype=np.int64)
-        dw = np.empty(len(g), dtype=np.int64)
+        dr = np.full(len(g), -1, dtype=np.int64)
+        dw = np.full(len(g), -1, dtype=np.int64)
         seen = {}
         for idx in orders[s]:                 # walk the send order; rows of one (s, g) block keep it
             ge = int(g[idx])
@@ -73,27 +80,36 @@ def dispatch(tokens, experts, nranks, experts_per_rank, hidden):
         ex = np.asarray(experts[s], dtype=np.int64)
         T, K = ex.shape
         tok = np.repeat(np.arange(T), K)
-        order = np.lexsort((tok, ex.reshape(-1)))
+        g = ex.reshape(-1)
+        order = np.lexsort((tok, g))
+        order = order[(g[order] >= 0) & (g[order] < nranks * experts_per_rank)]
         rows = np.asarray(tokens[s]).reshape(T, hidden)
         sends.append(rows[tok[order]].reshape(-1))
     return all_to_all(sends, splits, hidden)
 
 
-def combine_rows(y, w, dtype):
+def combine_rows(y, w, dtype, keep=None):
     """The weighted sum of one or more tokens' K expert rows.
 
-    y: [K, n, H] rows in storage type (bf16 as bit patterns), w: fp32 [n, K].
+    y: [K, n, H] rows in storage type (bf16 as bit patterns), w: fp32 [n, K],
+    keep: optional bool [n, K] (False: a dropped route, left out).
     Returns [n, H] in `dtype`: widen to fp32, p_k = fp32(w_k * y_k), then
-    ((p_0 + p_1) + p_2) + ... in fp32, then round to the row type."""
+    ((p_0 + p_1) + p_2) + ... in fp32 over the kept routes, then round to the
+    row type; zeros where no route is kept."""
     y = np.asarray(y)
     w = np.asarray(w, dtype=np.float32)
     K, n, H = y.shape
-    acc = None
+    keep = np.ones((n, K), dtype=bool) if keep is None else np.asarray(keep, dtype=bool)
+    acc = np.zeros((n, H), dtype=np.float32)
+    started = np.zeros(n, dtype=bool)
     with np.errstate(over="ignore", invalid="ignore"):
         for k in range(K):
             yk = _widen(y[k].reshape(-1), dtype).reshape(n, H)
             term = (w[:, k:k + 1] * yk).astype(np.float32)
-            acc = term if acc is None else (acc + term).astype(np.float32)
+            summed = (acc + term).astype(np.float32)
+            kk = keep[:, k]
+            acc = np.where((kk & started)[:, None], summed, np.where(kk[:, None], term, acc))
+            started |= kk
     return f32_to_bf16(acc) if dtype == "bf16" else acc.astype(np.float32)
 
 
@@ -107,10 +123,14 @@ def combine(expert_out, experts, weights, nranks, experts_per_rank, hidden, dtyp
     for s in range(nranks):
         w = np.asarray(weights[s], dtype=np.float32)
         T, K = w.shape
-        y = np.empty((K, T, hidden), dtype=np.asarray(expert_out[0]).dtype)
+        y = np.zeros((K, T, hidden), dtype=np.asarray(expert_out[0]).dtype)
+        keep = np.zeros((T, K), dtype=bool)
         for k in range(K):
             for t in range(T):
                 d, r = int(dest_rank[s][t * K + k]), int(dest_row[s][t * K + k])
+                if d < 0:
+                    continue
+                keep[t, k] = True
                 y[k, t] = np.asarray(expert_out[d])[r * hidden:(r + 1) * hidden]
-        outs.append(combine_rows(y, w, dtype).reshape(-1))
+        outs.append(combine_rows(y, w, dtype, keep).reshape(-1))
     return outs

@@ -198,3 +198,28 @@ def test_empty_source_and_no_copies():
     out = M.combine(recv, experts, [np.zeros((0, 2), np.float32), np.array([[0.5, 0.25]], np.float32)],
                     2, 1, 2, "fp32")
     assert len(out[0]) == 0 and list(out[1]) == [3.75, 4.5]
+
+
+def test_dropped_routes():
+    # expert ids outside [0, N*E) are dropped: the plan equals the plan without them
+    N, E = 2, 2
+    experts = [np.array([[3, -1], [4, 0], [1, 2]], np.int64), np.array([[-5, 7]], np.int64)]
+    kept = [np.array([[3], [0], [1]], np.int64), np.zeros((1, 0), np.int64)]
+    splits, dr, dw = M.route_plan(experts, N, E)
+    ref_splits, _, _ = M.route_plan([np.array([[3], [0], [1], [2]], np.int64), np.zeros((0, 1), np.int64)], N, E)
+    assert np.array_equal(splits, ref_splits)
+    assert list(dr[0]) == [1, -1, -1, 0, 0, 1] and list(dw[0][[1, 2]]) == [-1, -1]
+    assert list(dr[1]) == [-1, -1]
+    H = 2
+    toks = [np.array([1, 2, 3, 4, 5, 6], np.float32), np.array([7, 8], np.float32)]
+    recv = M.dispatch(toks, experts, N, E, H)
+    assert sum(len(r) for r in recv) == 4 * H
+    w = [np.full((3, 2), 0.5, np.float32), np.ones((1, 2), np.float32)]
+    out = M.combine(recv, experts, w, N, E, H, "fp32")
+    # token 0 keeps only k = 0; token 1 only k = 1; token 2 both; source 1's token none
+    assert list(out[0]) == [0.5, 1.0, 1.5, 2.0, 5.0, 6.0]
+    assert list(out[1]) == [0.0, 0.0] and not np.signbit(out[1]).any()
+    # a kept -0 product is the fold's start, not 0 + (-0)
+    y = np.array([[[0.0]], [[-0.0]]], np.float32)
+    got = M.combine_rows(y, np.ones((1, 2), np.float32), "fp32", keep=np.array([[False, True]]))
+    assert np.signbit(got[0, 0])
