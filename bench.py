@@ -16,7 +16,9 @@ is the dominant kernel's achieved bandwidth over the 8 TB/s HBM3E peak.
 Other workloads (--workload): ar_fp32_n4, ddp_llama7b, ddp_llama7b_zero_copy,
 fsdp_layer_n64, moe_a2a_n8 (the remaining parity configurations, measured the
 same way; the zero-copy DDP step all-reduces each bucket in place over the
-gradient tensors instead of packing and unpacking it).
+gradient tensors instead of packing and unpacking it), and moe_ep_n8 (the
+expert-parallel MoE data flow: routing plan, dispatch from token order and
+weighted combine back to token order, identity experts).
 """
 
 import argparse
@@ -32,11 +34,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective HBM GB/s (% of peak) for N=8 × 64 MiB bf16 all-reduce on 1 MI355X"
-KERNEL_SOURCES = ["collective_communication_reduction_amd/csrc/reduce.hip",
-                  "collective_communication_reduction_amd/csrc/movement.hip",
-                  "collective_communication_reduction_amd/csrc/bucket.hip",
-                  "collective_communication_reduction_amd/csrc/fold.h",
-                  "collective_communication_reduction_amd/csrc/device_common.h"]
+CSRC = "collective_communication_reduction_amd/csrc/"
+# Sources of each workload's dominant kernel: a committed profile's counters
+# stay valid while these files hash to the value recorded with them.
+KERNEL_SOURCES = {
+    "reduce": [CSRC + "reduce.hip", CSRC + "fold.h", CSRC + "device_common.h"],
+    "bucket": [CSRC + "bucket.hip", CSRC + "fold.h", CSRC + "device_common.h"],
+    "a2a": [CSRC + "movement.hip", CSRC + "device_common.h"],
+    "moe": [CSRC + "moe.hip", CSRC + "fold.h", CSRC + "device_common.h"],
+}
+WORKLOAD_KERNELS = {"ar_bf16_n8": "reduce", "ar_fp32_n4": "reduce", "ddp_llama7b": "reduce",
+                    "fsdp_layer_n64": "reduce", "ddp_llama7b_zero_copy": "bucket", "moe_a2a_n8": "a2a",
+                    "moe_ep_n8": "moe"}
 
 
 def parse():
@@ -46,7 +55,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ar_bf16_n8",
                    choices=["ar_bf16_n8", "ar_fp32_n4", "ddp_llama7b", "ddp_llama7b_zero_copy", "fsdp_layer_n64",
-                            "moe_a2a_n8"])
+                            "moe_a2a_n8", "moe_ep_n8"])
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--layout", default="arena", choices=["arena", "staggered", "separate"],
                    help="placement of the rank buffers in HBM")
@@ -58,9 +67,9 @@ def parse():
     return p.parse_args()
 
 
-def kernel_hash():
+def kernel_hash(workload):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[WORKLOAD_KERNELS[workload]]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -76,7 +85,7 @@ def traffic_from_profiles(workload):
     text = open(path, encoding="utf-8").read()
     m = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_(?:launch|step):\s*([0-9]+)", text)
-    if not m or not t or m.group(1) != kernel_hash():
+    if not m or not t or m.group(1) != kernel_hash(workload):
         return None
     return int(t.group(1))
 
@@ -407,6 +416,104 @@ class MoeWorkload(Workload):
         return run, 2 * int(sub.sum()) * h * 2, "oracle all-to-all of the first 4096 rows of each source, 256 of 4096 columns"
 
 
+class MoeEpWorkload(Workload):
+    """Expert-parallel MoE data flow, 8 ranks x 16384 tokens x 4096 bf16, top-2 of 64 experts, Zipf(1.1):
+    routing plan on the device, dispatch from token order, combine with the gate weights back to
+    token order.  The experts are the identity (their compute is not part of the data flow), so the
+    combine reads the dispatched rows."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+        import collective_communication_reduction_amd as gc
+        from gen import device as GD
+        from gen.workloads import WORKLOADS, route_tokens
+        self.gc = gc
+        cfg = WORKLOADS["moe_ep_n8"]
+        self.cfg = cfg
+        N, T, H, K = cfg["nranks"], cfg["tokens"], cfg["hidden"], cfg["topk"]
+        self.N, self.T, self.H, self.K, self.E = N, T, H, K, cfg["experts"] // N
+        self.name = "moe_ep_n8"
+        self.seed = args.seed
+        self.experts_host = [route_tokens(args.seed, s, T, cfg["experts"], K, cfg["zipf_s"]) for s in range(N)]
+        self.experts = [torch.from_numpy(e.reshape(-1).astype(np.int32)).cuda() for e in self.experts_host]
+        self.ntok = [T] * N
+        self.weights = [torch.empty(T * K, dtype=torch.float32, device="cuda") for _ in range(N)]
+        for s in range(N):
+            GD.fill_uniform_f32(self.weights[s], _keyed(args.seed, s, 3))
+        L = Layout(args, N)
+        self.layout = L.name()
+        self.tokens = L.buffers(T * H, torch.bfloat16)
+        for s in range(N):
+            GD.fill_normal_bf16(self.tokens[s], _keyed(args.seed, s), 1.0)
+        self.splits = torch.empty(N * N * self.E, dtype=torch.int64, device="cuda")
+        self.dest = [torch.empty(T * K * 2, dtype=torch.int32, device="cuda") for _ in range(N)]
+        self.scratch = torch.empty(gc.gc_moe_route_scratch_bytes(self.ntok, K, self.E), dtype=torch.uint8,
+                                   device="cuda")
+        # the receive buffers are sized from one routing plan (a real step reads the splits back too)
+        gc.gc_moe_route(self.experts, self.ntok, K, self.E, self.splits, self.dest, self.scratch)
+        self.recv_rows = [int(x) for x in self.splits.view(N, N, self.E).sum(dim=(0, 2)).cpu()]
+        recv_full = L.buffers(max(self.recv_rows) * H, torch.bfloat16)
+        self.recv = [recv_full[d][:self.recv_rows[d] * H] for d in range(N)]
+        self.out = L.buffers(T * H, torch.bfloat16)
+        self.row_bytes = H * 2
+        routes = N * T * K
+        self.route_bytes = routes * (4 + 8) + N * N * self.E * 8
+        self.dispatch_bytes = N * T * self.row_bytes + routes * (self.row_bytes + 8)
+        self.combine_bytes = routes * (self.row_bytes + 8 + 4) + N * T * self.row_bytes
+        self.bytes_per_step = self.route_bytes + self.dispatch_bytes + self.combine_bytes
+        self.dominant = "combine_kernel (inverse all-to-all + weighted un-permute)"
+        self.dominant_bytes = self.combine_bytes
+        self.frac_dst0 = self.recv_rows[0] / routes
+        torch.cuda.synchronize()
+
+    def route(self):
+        self.gc.gc_moe_route(self.experts, self.ntok, self.K, self.E, self.splits, self.dest, self.scratch)
+
+    def dispatch(self):
+        self.gc.gc_moe_dispatch(self.tokens, self.ntok, self.dest, self.K, self.row_bytes, self.recv,
+                                self.recv_rows)
+
+    def combine(self):
+        self.gc.gc_moe_combine(self.recv, self.recv_rows, self.dest, self.weights, self.ntok, self.K, self.H,
+                               "bf16", self.out)
+
+    def step(self, k):
+        self.route()
+        self.dispatch()
+        self.combine()
+
+    def dominant_launch(self, k):
+        self.combine()
+
+    def config(self):
+        c = self.cfg
+        return {"workload": self.name, "nranks": self.N, "tokens": self.T, "hidden": self.H,
+                "experts": c["experts"], "topk": self.K, "zipf_s": c["zipf_s"], "storage": "bf16",
+                "frac_rows_to_rank0": round(self.frac_dst0, 4), "experts_compute": "identity",
+                "layout": self.layout}
+
+    def cpu_sample(self, seed):
+        import numpy as np
+        from gen import host as G
+        from oracle import moe as OM
+        # the first 4096 tokens of every source, 1024 of the 4096 hidden values
+        t, h, K = 4096, 1024, self.K
+        ex = [e[:t] for e in self.experts_host]
+        idx = (np.arange(t, dtype=np.uint64)[:, None] * np.uint64(self.H) + np.arange(h, dtype=np.uint64)).reshape(-1)
+        toks = [G.normal_bf16(_keyed(seed, s), idx, 1.0) for s in range(self.N)]
+        w = [G.uniform_f32(_keyed(seed, s, 3), np.arange(t * K, dtype=np.uint64)).reshape(t, K)
+             for s in range(self.N)]
+
+        def run():
+            recv = OM.dispatch(toks, ex, self.N, self.E, h)
+            return OM.combine(recv, ex, w, self.N, self.E, h, "bf16")
+        routes = self.N * t * K
+        nbytes = routes * 12 + self.N * t * h * 2 + routes * (h * 2 + 8) + routes * (h * 2 + 12) + self.N * t * h * 2
+        return run, nbytes, (f"oracle routing plan + dispatch + combine of the first {t} tokens of each source, "
+                             f"the first {h} of {self.H} hidden values")
+
+
 def make(args):
     if args.workload in ("ar_bf16_n8", "ar_fp32_n4"):
         from gen.workloads import WORKLOADS
@@ -418,6 +525,8 @@ def make(args):
         return DdpWorkload(args, zero_copy=True)
     if args.workload == "fsdp_layer_n64":
         return FsdpWorkload(args)
+    if args.workload == "moe_ep_n8":
+        return MoeEpWorkload(args)
     return MoeWorkload(args)
 
 

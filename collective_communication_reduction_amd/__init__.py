@@ -71,6 +71,11 @@ _c_ag = _sig("gc_all_gather", _int, _VPP, _VPP, _sz, _int, _int, _vp)
 _c_ar_scratch = _sig("gc_all_reduce_scratch_bytes", _sz, _sz, _int, _int, _int)
 _c_ar = _sig("gc_all_reduce", _int, _VPP, _VPP, _sz, _int, _int, _int, _int, _int, _vp, _sz, _vp)
 _c_a2a = _sig("gc_all_to_all", _int, _VPP, _VPP, ctypes.POINTER(ctypes.c_int64), _int, _int, _sz, _vp)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_c_moe_scratch = _sig("gc_moe_route_scratch_bytes", _sz, _I64P, _int, _int, _int)
+_c_moe_route = _sig("gc_moe_route", _int, _VPP, _I64P, _int, _int, _int, _vp, _VPP, _vp, _sz, _vp)
+_c_moe_dispatch = _sig("gc_moe_dispatch", _int, _VPP, _I64P, _VPP, _int, _int, _sz, _VPP, _I64P, _vp)
+_c_moe_combine = _sig("gc_moe_combine", _int, _VPP, _I64P, _VPP, _VPP, _I64P, _int, _int, _sz, _int, _VPP, _vp)
 _c_plan_create = _sig("gc_bucket_plan_create", _int, ctypes.POINTER(ctypes.c_size_t), _int, _int, _sz, _int, _sz,
                       ctypes.POINTER(_vp))
 _c_plan_query = _sig("gc_bucket_plan_query", _int, _vp, ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_size_t),
@@ -240,6 +245,44 @@ def gc_all_to_all(send, recv, splits, row_bytes, stream=None):
     _check(_c_a2a(_ptr_array(send), _ptr_array(recv), sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, e,
                   int(row_bytes), _stream(stream, _first(send))), "gc_all_to_all")
     return recv
+
+
+def _i64_array(xs):
+    xs = [int(x) for x in xs]
+    return (ctypes.c_int64 * max(1, len(xs)))(*xs)
+
+
+def gc_moe_route_scratch_bytes(ntokens, topk, experts_per_rank):
+    """Scratch bytes gc_moe_route needs for these per-source token counts (0 if the sizes are invalid)."""
+    return int(_c_moe_scratch(_i64_array(ntokens), len(ntokens), int(topk), int(experts_per_rank)))
+
+
+def gc_moe_route(experts, ntokens, topk, experts_per_rank, splits, dest, scratch, scratch_bytes=None, stream=None):
+    """MoE routing plan on the device.  experts[s]: int32 [ntokens[s] * topk] global expert ids;
+    splits: int64 [N*N*E] out; dest[s]: int32 [ntokens[s] * topk * 2] (rank, row) out."""
+    n = len(ntokens)
+    if scratch_bytes is None:
+        scratch_bytes = scratch.numel() * scratch.element_size()
+    _check(_c_moe_route(_ptr_array(experts), _i64_array(ntokens), n, int(topk), int(experts_per_rank),
+                        _addr(splits), _ptr_array(dest), _addr(scratch), int(scratch_bytes),
+                        _stream(stream, splits)), "gc_moe_route")
+    return splits, dest
+
+
+def gc_moe_dispatch(tokens, ntokens, dest, topk, row_bytes, recv, recv_rows, stream=None):
+    """Copy every token row of every source to the receive rows its routes name."""
+    _check(_c_moe_dispatch(_ptr_array(tokens), _i64_array(ntokens), _ptr_array(dest), len(ntokens), int(topk),
+                           int(row_bytes), _ptr_array(recv), _i64_array(recv_rows),
+                           _stream(stream, _first(recv))), "gc_moe_dispatch")
+    return recv
+
+
+def gc_moe_combine(expert_out, expert_rows, dest, weights, ntokens, topk, hidden, dtype, out, stream=None):
+    """out[s][t] = sum_k weights[s][t*topk + k] * expert_out[rank][row] over the routes of token t."""
+    _check(_c_moe_combine(_ptr_array(expert_out), _i64_array(expert_rows), _ptr_array(dest), _ptr_array(weights),
+                          _i64_array(ntokens), len(ntokens), int(topk), int(hidden), _dtype_code(dtype),
+                          _ptr_array(out), _stream(stream, _first(out))), "gc_moe_combine")
+    return out
 
 
 # ------------------------------------------------------------------ HBM layout

@@ -280,6 +280,148 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
   return GC_OK;
 }
 
+// ------------------------------------------------------------------------ MoE
+
+namespace {
+
+constexpr int kMoeMaxTopk = 8;
+constexpr int kMoeMaxBins = 8192;
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// Tiling of the routing plan: routes per tile, total tiles, scratch bytes.
+struct MoeRouteGeom {
+  int32_t tile = 0;
+  int64_t tiles = 0;
+  int64_t routes = 0;
+  uint64_t counts_bytes = 0;
+  uint64_t bytes = 0;
+};
+
+gc_status moe_route_geom(const int64_t* ntokens, int nranks, int topk, int E, MoeRouteGeom& g) {
+  GC_TRY(check_ranks(nranks));
+  if (!ntokens || topk < 1 || E < 1) return GC_ERR_INVALID_ARG;
+  if (topk > kMoeMaxTopk || static_cast<int64_t>(nranks) * E > kMoeMaxBins) return GC_ERR_UNSUPPORTED;
+  const int64_t nbins = static_cast<int64_t>(nranks) * E;
+  g.tile = static_cast<int32_t>(std::max<int64_t>(512, (nbins + 63) / 64 * 64));
+  for (int s = 0; s < nranks; ++s) {
+    if (ntokens[s] < 0) return GC_ERR_INVALID_ARG;
+    if (ntokens[s] >= (int64_t(1) << 31)) return GC_ERR_UNSUPPORTED;
+    const int64_t r = ntokens[s] * topk;
+    g.routes += r;
+    if (g.routes >= (int64_t(1) << 31)) return GC_ERR_UNSUPPORTED;
+    g.tiles += (r + g.tile - 1) / g.tile;
+  }
+  g.counts_bytes = align256(static_cast<uint64_t>(g.tiles) * nbins * 4);
+  g.bytes = g.counts_bytes + align256(static_cast<uint64_t>(nbins) * nranks * 4);
+  return GC_OK;
+}
+
+}  // namespace
+
+extern "C" size_t gc_moe_route_scratch_bytes(const int64_t* ntokens, int nranks, int topk, int experts_per_rank) {
+  MoeRouteGeom g;
+  return moe_route_geom(ntokens, nranks, topk, experts_per_rank, g) == GC_OK ? g.bytes : 0;
+}
+
+extern "C" gc_status gc_moe_route(const int32_t* const* experts, const int64_t* ntokens, int nranks, int topk,
+                                  int experts_per_rank, int64_t* splits, int32_t* const* dest, void* scratch,
+                                  size_t scratch_bytes, hipStream_t stream) {
+  MoeRouteGeom g;
+  GC_TRY(moe_route_geom(ntokens, nranks, topk, experts_per_rank, g));
+  const int N = nranks, E = experts_per_rank;
+  if (!experts || !dest || !splits || addr(splits) % 8) return GC_ERR_INVALID_ARG;
+  if (!scratch || addr(scratch) % 256 || scratch_bytes < g.bytes) return GC_ERR_INVALID_ARG;
+  std::vector<Span> outs{span(splits, static_cast<uint64_t>(N) * N * E * 8), span(scratch, g.bytes)};
+  std::vector<Span> ins;
+  std::vector<int64_t> routes(N);
+  for (int s = 0; s < N; ++s) {
+    routes[s] = ntokens[s] * topk;
+    if (!routes[s]) continue;
+    if (!experts[s] || addr(experts[s]) % 4 || !dest[s] || addr(dest[s]) % 8) return GC_ERR_INVALID_ARG;
+    ins.push_back(span(experts[s], routes[s] * 4));
+    outs.push_back(span(dest[s], routes[s] * 8));
+  }
+  if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (overlaps(o, i)) return GC_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(scratch);
+  gci::MoeRouteCall call{experts, dest, routes.data(), N, E, g.tile,
+                         reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base + g.counts_bytes),
+                         splits, stream};
+  return gci::launch_moe_route(call);
+}
+
+namespace {
+
+// Checks shared by dispatch and combine: row buffers of src (src_rows each),
+// dst (dst_rows each) and the per-source route tables.
+gc_status moe_move_check(const void* const* src, const int64_t* src_rows, void* const* dst, const int64_t* dst_rows,
+                         const int32_t* const* dest, const float* const* weights, const int64_t* ntokens,
+                         int nranks, int topk, uint64_t row_bytes) {
+  GC_TRY(check_ranks(nranks));
+  if (!src || !src_rows || !dst || !dst_rows || !dest || !ntokens || topk < 1 || row_bytes == 0)
+    return GC_ERR_INVALID_ARG;
+  if (topk > kMoeMaxTopk) return GC_ERR_UNSUPPORTED;
+  std::vector<Span> outs, ins;
+  int64_t routes = 0;
+  for (int r = 0; r < nranks; ++r) {
+    if (ntokens[r] < 0 || src_rows[r] < 0 || dst_rows[r] < 0) return GC_ERR_INVALID_ARG;
+    if (ntokens[r] >= (int64_t(1) << 31) || src_rows[r] >= (int64_t(1) << 31) || dst_rows[r] >= (int64_t(1) << 31))
+      return GC_ERR_UNSUPPORTED;
+    routes += ntokens[r] * topk;
+    if (routes >= (int64_t(1) << 31)) return GC_ERR_UNSUPPORTED;
+    if (mul_overflows(static_cast<uint64_t>(src_rows[r]), row_bytes) ||
+        mul_overflows(static_cast<uint64_t>(dst_rows[r]), row_bytes))
+      return GC_ERR_INVALID_ARG;
+    if ((src_rows[r] && !src[r]) || (dst_rows[r] && !dst[r])) return GC_ERR_INVALID_ARG;
+    outs.push_back(span(dst[r], dst_rows[r] * row_bytes));
+    ins.push_back(span(src[r], src_rows[r] * row_bytes));
+    if (ntokens[r]) {
+      if (!dest[r] || addr(dest[r]) % 8) return GC_ERR_INVALID_ARG;
+      ins.push_back(span(dest[r], ntokens[r] * topk * 8));
+      if (weights) {
+        if (!weights[r] || addr(weights[r]) % 4) return GC_ERR_INVALID_ARG;
+        ins.push_back(span(weights[r], ntokens[r] * topk * 4));
+      }
+    }
+  }
+  if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (overlaps(o, i)) return GC_ERR_INVALID_ARG;
+  return GC_OK;
+}
+
+}  // namespace
+
+extern "C" gc_status gc_moe_dispatch(const void* const* tokens, const int64_t* ntokens, const int32_t* const* dest,
+                                     int nranks, int topk, size_t row_bytes, void* const* recv,
+                                     const int64_t* recv_rows, hipStream_t stream) {
+  GC_TRY(moe_move_check(tokens, ntokens, recv, recv_rows, dest, nullptr, ntokens, nranks, topk, row_bytes));
+  gci::MoeMoveCall call{tokens, ntokens, dest, nullptr, recv, recv_rows, ntokens, nranks, topk, row_bytes,
+                        GC_BF16, stream};
+  return gci::launch_moe_dispatch(call);
+}
+
+extern "C" gc_status gc_moe_combine(const void* const* expert_out, const int64_t* expert_rows,
+                                    const int32_t* const* dest, const float* const* weights,
+                                    const int64_t* ntokens, int nranks, int topk, size_t hidden, gc_dtype t,
+                                    void* const* out, hipStream_t stream) {
+  if (!valid_dtype(t) || !weights) return GC_ERR_INVALID_ARG;
+  if (t == GC_INT32) return GC_ERR_UNSUPPORTED;
+  if (hidden == 0 || mul_overflows(hidden, elem_bytes(t))) return GC_ERR_INVALID_ARG;
+  const uint64_t row_bytes = hidden * elem_bytes(t);
+  GC_TRY(moe_move_check(expert_out, expert_rows, out, ntokens, dest, weights, ntokens, nranks, topk, row_bytes));
+  for (int r = 0; r < nranks; ++r)
+    if ((expert_rows[r] && addr(expert_out[r]) % elem_bytes(t)) || (ntokens[r] && addr(out[r]) % elem_bytes(t)))
+      return GC_ERR_INVALID_ARG;
+  gci::MoeMoveCall call{expert_out, expert_rows, dest, weights, out, ntokens, ntokens, nranks, topk, row_bytes,
+                        t, stream};
+  return gci::launch_moe_combine(call);
+}
+
 // ---------------------------------------------------------------- bucket plan
 
 struct gc_bucket_plan {

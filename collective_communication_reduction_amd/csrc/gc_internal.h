@@ -92,4 +92,41 @@ constexpr int kA2AMaxBlocks = 512;
 
 gc_status launch_all_to_all(const A2ACall& call);
 
+// MoE routing plan (see gc_moe_route).  Routes of source s are cut into tiles
+// of `tile` routes; counts holds [tiles][nranks * experts_per_rank] int32 and
+// roff [nranks][nranks * experts_per_rank] int32 of scratch.
+struct MoeRouteCall {
+  const int32_t* const* experts;
+  int32_t* const* dest;
+  const int64_t* routes;  // [nranks] tokens * topk
+  int nranks;
+  int experts_per_rank;
+  int32_t tile;
+  int32_t* counts;
+  int32_t* roff;
+  int64_t* splits;
+  hipStream_t stream;
+};
+
+// MoE dispatch (src = token rows, dst = receive buffers) or combine
+// (src = expert outputs in the receive layout, dst = token rows).
+struct MoeMoveCall {
+  const void* const* src;
+  const int64_t* src_rows;     // rows of each src buffer
+  const int32_t* const* dest;  // per source: [tokens * topk] (rank, row) pairs
+  const float* const* weights; // combine only
+  void* const* dst;
+  const int64_t* dst_rows;     // rows of each dst buffer
+  const int64_t* tokens;       // [nranks] tokens per source
+  int nranks;
+  int topk;
+  uint64_t row_bytes;
+  gc_dtype t;                  // combine only
+  hipStream_t stream;
+};
+
+gc_status launch_moe_route(const MoeRouteCall& call);
+gc_status launch_moe_dispatch(const MoeMoveCall& call);
+gc_status launch_moe_combine(const MoeMoveCall& call);
+
 }  // namespace gci

@@ -1,0 +1,480 @@
+// Expert-parallel MoE data flow around the all-to-all, for gfx950 (DTLM §8
+// "专家并行和 MoE 通信": router top-k, pack by target expert / rank, dispatch,
+// local experts, combine back, restore token order).
+//
+//   route     the routing plan, on the device: from each source's top-k expert
+//             ids to the split table and, per (token, k), the rank and row its
+//             copy occupies in the receive layout (by local expert, then
+//             source, then token).  Three small kernels: a stable in-tile rank
+//             per route (one wavefront per tile, ballot-grouped by expert), a
+//             per-destination scan of the tile counts, and the final row sums.
+//   dispatch  the pack fused into the all-to-all: each token row is read once
+//             and written to its K destinations (an HBM stream, no arithmetic).
+//   combine   the inverse all-to-all fused with the weighted un-permute: each
+//             output row gathers its K expert rows, sums w_k * y_k in fp32
+//             (k = 0 first, every product rounded to fp32), rounds once.
+//
+// Route entries whose rank or row falls outside the destination buffers are
+// skipped by dispatch and combine, so malformed plans cannot fault.
+
+#include <algorithm>
+#include <type_traits>
+
+#include "fold.h"
+#include "gc_internal.h"
+
+namespace {
+
+using namespace gcdev;
+
+// ------------------------------------------------------------ routing plan
+
+constexpr int kWave = 64;
+
+template <int P>
+struct RouteArgs {
+  const int32_t* experts[P];  // [routes_s] global expert ids, token-major (t * K + k)
+  int2* dest[P];              // [routes_s] (rank, row); (expert, in-tile rank) in between kernels
+  int64_t routes[P];          // tokens_s * K
+  int32_t tile0[P + 1];       // first tile of each source
+  int32_t* counts;            // [tiles][nbins] per-tile counts, then exclusive prefixes over tiles
+  int32_t* roff;              // [N][nbins] receive-row offset of block (s, expert)
+  int64_t* splits;            // [N][N][E]
+  int32_t tile;               // routes per tile
+  int32_t N, E, nbins;
+};
+
+template <int P>
+__device__ __forceinline__ int source_of(const int32_t (&first)[P + 1], int N, int32_t b) {
+  int s = 0;
+  while (s + 1 < N && first[s + 1] <= b) ++s;
+  return s;
+}
+
+// One wavefront per tile: the rank of every route among the tile's earlier
+// routes to the same expert, grouping lanes that share an expert by ballot.
+template <int P>
+__global__ void __launch_bounds__(kWave) route_count_kernel(const RouteArgs<P> a) {
+  extern __shared__ int32_t cnt[];
+  const int32_t b = blockIdx.x;
+  const int s = source_of<P>(a.tile0, a.N, b);
+  const int64_t lo = static_cast<int64_t>(b - a.tile0[s]) * a.tile;
+  const int64_t n = min<int64_t>(a.tile, a.routes[s] - lo);
+  const int lane = threadIdx.x;
+  for (int i = lane; i < a.nbins; i += kWave) cnt[i] = 0;
+  __syncthreads();
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int64_t c0 = 0; c0 < n; c0 += kWave) {
+    const int64_t i = c0 + lane;
+    const bool in = i < n;
+    const int32_t g = in ? a.experts[s][lo + i] : -1;
+    const bool valid = in && g >= 0 && g < a.nbins;
+    uint64_t pending = __ballot(valid);
+    int32_t rank = -1;
+    while (pending) {
+      const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+      const int32_t v = __shfl(g, leader);
+      const uint64_t same = __ballot(valid && g == v);
+      const int32_t base = cnt[v];
+      if (valid && g == v) rank = base + __popcll(same & below);
+      if (lane == leader) cnt[v] = base + __popcll(same);
+      pending &= ~same;
+    }
+    if (in) a.dest[s][lo + i] = valid ? make_int2(g, rank) : make_int2(-1, -1);
+  }
+  __syncthreads();
+  for (int i = lane; i < a.nbins; i += kWave) a.counts[static_cast<int64_t>(b) * a.nbins + i] = cnt[i];
+}
+
+// Exclusive scan of one value per thread over a workgroup of kThreads.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* lds, int32_t& total) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  int32_t x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) lds[wid] = x;
+  __syncthreads();
+  int32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    const int32_t t = lds[w];
+    off += w < wid ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return off + x - v;
+}
+
+// One workgroup per destination d: per (source, local expert) the tile
+// counts become exclusive prefixes and their total the split; the receive
+// offsets follow by scanning the blocks in (expert, source) order.
+template <int P>
+__global__ void __launch_bounds__(kThreads) route_scan_kernel(const RouteArgs<P> a) {
+  __shared__ int32_t lds[kThreads / kWave];
+  const int d = blockIdx.x;
+  const int items = a.E * a.N;
+  int32_t carry = 0;
+  for (int base = 0; base < items; base += kThreads) {
+    const int i = base + threadIdx.x;
+    int32_t total = 0;
+    int s = 0, g = 0;
+    if (i < items) {
+      const int e = i / a.N;
+      s = i - e * a.N;
+      g = d * a.E + e;
+      for (int32_t t = a.tile0[s]; t < a.tile0[s + 1]; ++t) {
+        int32_t* c = a.counts + static_cast<int64_t>(t) * a.nbins + g;
+        const int32_t v = *c;
+        *c = total;
+        total += v;
+      }
+      a.splits[(static_cast<int64_t>(s) * a.N + d) * a.E + e] = total;
+    }
+    int32_t sum;
+    const int32_t excl = block_exclusive_scan(total, lds, sum);
+    if (i < items) a.roff[static_cast<int64_t>(s) * a.nbins + g] = carry + excl;
+    carry += sum;
+  }
+}
+
+template <int P>
+__global__ void __launch_bounds__(kThreads) route_final_kernel(const RouteArgs<P> a) {
+  const int32_t b = blockIdx.x;
+  const int s = source_of<P>(a.tile0, a.N, b);
+  const int64_t lo = static_cast<int64_t>(b - a.tile0[s]) * a.tile;
+  const int64_t n = min<int64_t>(a.tile, a.routes[s] - lo);
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+    const int2 p = a.dest[s][lo + i];
+    if (p.x < 0) continue;
+    const int32_t row = a.roff[static_cast<int64_t>(s) * a.nbins + p.x] +
+                        a.counts[static_cast<int64_t>(b) * a.nbins + p.x] + p.y;
+    a.dest[s][lo + i] = make_int2(p.x / a.E, row);
+  }
+}
+
+// ------------------------------------------------------- dispatch / combine
+//
+// Rows are cut into units (a 16-byte vector, or one element / byte when the
+// rows or buffers are not 16-byte aligned).  S = 2^lanes_log2 lanes work on a
+// row, two units per lane per step; a workgroup holds kThreads / S rows.
+
+template <int P>
+struct DispatchArgs {
+  const char* tok[P];      // [tokens_s][R units]
+  const int2* dest[P];     // [tokens_s * K] (rank, row)
+  char* recv[P];           // [recv_rows_d][R units]
+  int64_t recv_rows[P];
+  int64_t ntok[P];
+  int32_t grp0[P + 1];     // first row group of each source
+  uint64_t R;              // units per row
+  int32_t N, K, lanes_log2;
+};
+
+template <class T>
+__device__ __forceinline__ T ld_unit(const T* p) {
+  if constexpr (sizeof(T) == 16) return ld16(p);
+  else return __builtin_nontemporal_load(p);
+}
+template <class T>
+__device__ __forceinline__ void st_unit(T* p, T v) {
+  if constexpr (sizeof(T) == 16) st16(p, v);
+  else __builtin_nontemporal_store(v, p);
+}
+
+// Rank and row of route (t, k) as a unit pointer into its destination, or
+// nullptr when the entry lies outside the destination buffers.
+template <class T, int P>
+__device__ __forceinline__ T* route_row(char* const (&buf)[P], const int64_t (&rows)[P], int N, int2 p,
+                                        uint64_t R) {
+  if (p.x < 0 || p.x >= N || p.y < 0 || p.y >= rows[p.x]) return nullptr;
+  return reinterpret_cast<T*>(buf[p.x]) + static_cast<uint64_t>(p.y) * R;
+}
+
+template <class T, int P>
+__global__ void __launch_bounds__(kThreads) dispatch_kernel(const DispatchArgs<P> a) {
+  const int S = 1 << a.lanes_log2;
+  const int sub = threadIdx.x >> a.lanes_log2, lane = threadIdx.x & (S - 1);
+  const int G = kThreads >> a.lanes_log2;
+  const int32_t ngroups = a.grp0[a.N];
+  for (int32_t b = blockIdx.x; b < ngroups; b += gridDim.x) {
+    const int s = source_of<P>(a.grp0, a.N, b);
+    const int64_t t = static_cast<int64_t>(b - a.grp0[s]) * G + sub;
+    if (t >= a.ntok[s]) continue;
+    const T* src = reinterpret_cast<const T*>(a.tok[s]) + static_cast<uint64_t>(t) * a.R;
+    const int2* dst = a.dest[s] + t * a.K;
+    for (uint64_t c = lane; c < a.R; c += 2 * S) {
+      const bool two = c + S < a.R;
+      const T v0 = ld_unit(src + c);
+      const T v1 = ld_unit(src + (two ? c + S : c));  // clamped: no exec-masked load
+      for (int k = 0; k < a.K; ++k) {
+        T* out = route_row<T, P>(a.recv, a.recv_rows, a.N, dst[k], a.R);
+        if (!out) continue;
+        st_unit(out + c, v0);
+        if (two) st_unit(out + c + S, v1);
+      }
+    }
+  }
+}
+
+template <int P>
+struct CombineArgs {
+  char* y[P];              // expert outputs in the receive layout (read only)
+  int64_t y_rows[P];
+  const int2* dest[P];     // [tokens_s * K]
+  const float* w[P];       // [tokens_s * K] gate weights
+  char* out[P];            // [tokens_s][R units]
+  int64_t ntok[P];
+  int32_t grp0[P + 1];
+  uint64_t R;
+  int32_t N, K, lanes_log2;
+};
+
+// One unit of K weighted rows: 16-byte vectors of In::VE elements, or single elements.
+template <class In, bool VEC>
+struct Unit;
+
+template <class In>
+struct Unit<In, true> {
+  typedef u32x4 T;
+  static constexpr int VE = In::VE;
+  __device__ static __forceinline__ void widen(const T& v, float (&x)[VE]) { unpack<In>(v, x); }
+  __device__ static __forceinline__ T narrow(const float (&x)[VE]) {
+    const Words<typename std::conditional<In::ES == 2, OutBf16, OutF32>::type, VE> r =
+        pack<typename std::conditional<In::ES == 2, OutBf16, OutF32>::type, VE>(x);
+    return u32x4{r.w[0], r.w[1], r.w[2], r.w[3]};
+  }
+};
+
+template <>
+struct Unit<InBf16, false> {
+  typedef uint16_t T;
+  static constexpr int VE = 1;
+  __device__ static __forceinline__ void widen(const T& v, float (&x)[1]) {
+    x[0] = __uint_as_float(static_cast<uint32_t>(v) << 16);
+  }
+  __device__ static __forceinline__ T narrow(const float (&x)[1]) { return static_cast<T>(bf16_bits(x[0])); }
+};
+
+template <>
+struct Unit<InF32, false> {
+  typedef uint32_t T;
+  static constexpr int VE = 1;
+  __device__ static __forceinline__ void widen(const T& v, float (&x)[1]) { x[0] = __uint_as_float(v); }
+  __device__ static __forceinline__ T narrow(const float (&x)[1]) { return __float_as_uint(x[0]); }
+};
+
+// acc = w * y (first valid route) or acc + w * y, each product rounded to fp32.
+template <int VE>
+__device__ __forceinline__ void accumulate(float (&acc)[VE], const float (&y)[VE], float w, bool first) {
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    const float p = w * y[e];
+    acc[e] = first ? p : acc[e] + p;
+  }
+}
+
+// KT > 0: K == KT known at compile time (all K loads of a step in flight at once).
+template <class In, bool VEC, int KT, int P>
+__global__ void __launch_bounds__(kThreads) combine_kernel(const CombineArgs<P> a) {
+  typedef Unit<In, VEC> U;
+  typedef typename U::T T;
+  constexpr int VE = U::VE;
+  constexpr int KB = KT > 0 ? KT : 1;  // routes held per batch
+  const int K = KT > 0 ? KT : a.K;
+  const int S = 1 << a.lanes_log2;
+  const int sub = threadIdx.x >> a.lanes_log2, lane = threadIdx.x & (S - 1);
+  const int G = kThreads >> a.lanes_log2;
+  const int32_t ngroups = a.grp0[a.N];
+  for (int32_t b = blockIdx.x; b < ngroups; b += gridDim.x) {
+    const int s = source_of<P>(a.grp0, a.N, b);
+    const int64_t t = static_cast<int64_t>(b - a.grp0[s]) * G + sub;
+    if (t >= a.ntok[s]) continue;
+    const int2* routes = a.dest[s] + t * K;
+    const float* wt = a.w[s] + t * K;
+    T* out = reinterpret_cast<T*>(a.out[s]) + static_cast<uint64_t>(t) * a.R;
+    for (uint64_t c = lane; c < a.R; c += 2 * S) {
+      const bool two = c + S < a.R;
+      const uint64_t c1 = two ? c + S : c;
+      float acc0[VE], acc1[VE];
+      bool any = false;
+      for (int k0 = 0; k0 < K; k0 += KB) {
+        T v0[KB], v1[KB];
+        bool ok[KB];
+        float wk[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          const T* row = route_row<T, P>(a.y, a.y_rows, a.N, routes[k0 + j], a.R);
+          ok[j] = row != nullptr;
+          wk[j] = wt[k0 + j];
+          if (ok[j]) {
+            v0[j] = ld_unit(row + c);
+            v1[j] = ld_unit(row + c1);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          if (!ok[j]) continue;
+          float y0[VE], y1[VE];
+          U::widen(v0[j], y0);
+          U::widen(v1[j], y1);
+          accumulate(acc0, y0, wk[j], !any);
+          accumulate(acc1, y1, wk[j], !any);
+          any = true;
+        }
+      }
+      if (!any) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc0[e] = acc1[e] = 0.0f;
+      }
+      st_unit(out + c, U::narrow(acc0));
+      if (two) st_unit(out + c + S, U::narrow(acc1));
+    }
+  }
+}
+
+// ------------------------------------------------------------ host side
+
+#ifndef GC_MOE_MAX_GRID
+#define GC_MOE_MAX_GRID (1u << 20)
+#endif
+
+template <class Kern, class A>
+gc_status launch(Kern kernel, const A& args, uint32_t grid, uint32_t threads, size_t lds, hipStream_t stream) {
+  void* params[] = {const_cast<A*>(&args)};
+  return gci::hip_status(hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(std::max(1u, grid)),
+                                         dim3(threads), params, lds, stream));
+}
+
+uint64_t addr(const void* p) { return reinterpret_cast<uint64_t>(p); }
+
+// Lanes per row: half the row's units rounded up to a power of two, 1..kThreads.
+int lanes_log2_for(uint64_t R) {
+  int l = 0;
+  while (l < 8 && (uint64_t(1) << (l + 1)) < R) ++l;
+  return l;
+}
+
+template <int P>
+void fill_groups(int32_t (&grp0)[P + 1], int64_t (&ntok)[P], const int64_t* tokens, int N, int G) {
+  int64_t run = 0;
+  for (int s = 0; s < N; ++s) {
+    grp0[s] = static_cast<int32_t>(run);
+    ntok[s] = tokens[s];
+    run += (tokens[s] + G - 1) / G;
+  }
+  for (int s = N; s <= P; ++s) grp0[s] = static_cast<int32_t>(run);
+}
+
+template <int P>
+gc_status route_impl(const gci::MoeRouteCall& c) {
+  RouteArgs<P> a{};
+  int32_t tiles = 0;
+  for (int s = 0; s < c.nranks; ++s) {
+    a.experts[s] = c.experts[s];
+    a.dest[s] = reinterpret_cast<int2*>(c.dest[s]);
+    a.routes[s] = c.routes[s];
+    a.tile0[s] = tiles;
+    tiles += static_cast<int32_t>((c.routes[s] + c.tile - 1) / c.tile);
+  }
+  for (int s = c.nranks; s <= P; ++s) a.tile0[s] = tiles;
+  a.counts = c.counts;
+  a.roff = c.roff;
+  a.splits = c.splits;
+  a.tile = c.tile;
+  a.N = c.nranks;
+  a.E = c.experts_per_rank;
+  a.nbins = c.nranks * c.experts_per_rank;
+  const size_t lds = static_cast<size_t>(a.nbins) * sizeof(int32_t);
+  if (tiles > 0) {
+    const gc_status st = launch(route_count_kernel<P>, a, tiles, kWave, lds, c.stream);
+    if (st != GC_OK) return st;
+  }
+  gc_status st = launch(route_scan_kernel<P>, a, c.nranks, kThreads, 0, c.stream);
+  if (st != GC_OK || tiles == 0) return st;
+  return launch(route_final_kernel<P>, a, tiles, kThreads, 0, c.stream);
+}
+
+template <class T, int P>
+gc_status dispatch_impl(const gci::MoeMoveCall& c, uint64_t R) {
+  DispatchArgs<P> a{};
+  for (int s = 0; s < c.nranks; ++s) {
+    a.tok[s] = static_cast<const char*>(c.src[s]);
+    a.dest[s] = reinterpret_cast<const int2*>(c.dest[s]);
+    a.recv[s] = static_cast<char*>(c.dst[s]);
+    a.recv_rows[s] = c.dst_rows[s];
+  }
+  a.R = R;
+  a.N = c.nranks;
+  a.K = c.topk;
+  a.lanes_log2 = lanes_log2_for(R);
+  fill_groups<P>(a.grp0, a.ntok, c.tokens, c.nranks, kThreads >> a.lanes_log2);
+  if (a.grp0[c.nranks] == 0) return GC_OK;
+  const uint32_t grid = std::min<uint32_t>(a.grp0[c.nranks], GC_MOE_MAX_GRID);
+  return launch(dispatch_kernel<T, P>, a, grid, kThreads, 0, c.stream);
+}
+
+template <class In, bool VEC, int P>
+gc_status combine_impl(const gci::MoeMoveCall& c, uint64_t R) {
+  CombineArgs<P> a{};
+  for (int s = 0; s < c.nranks; ++s) {
+    a.y[s] = static_cast<char*>(const_cast<void*>(c.src[s]));
+    a.y_rows[s] = c.src_rows[s];
+    a.dest[s] = reinterpret_cast<const int2*>(c.dest[s]);
+    a.w[s] = c.weights[s];
+    a.out[s] = static_cast<char*>(c.dst[s]);
+  }
+  a.R = R;
+  a.N = c.nranks;
+  a.K = c.topk;
+  a.lanes_log2 = lanes_log2_for(R);
+  fill_groups<P>(a.grp0, a.ntok, c.tokens, c.nranks, kThreads >> a.lanes_log2);
+  if (a.grp0[c.nranks] == 0) return GC_OK;
+  const uint32_t grid = std::min<uint32_t>(a.grp0[c.nranks], GC_MOE_MAX_GRID);
+  switch (c.topk) {
+    case 1: return launch(combine_kernel<In, VEC, 1, P>, a, grid, kThreads, 0, c.stream);
+    case 2: return launch(combine_kernel<In, VEC, 2, P>, a, grid, kThreads, 0, c.stream);
+    default: return launch(combine_kernel<In, VEC, 0, P>, a, grid, kThreads, 0, c.stream);
+  }
+}
+
+template <int P>
+gc_status dispatch_any(const gci::MoeMoveCall& c) {
+  uint64_t m = c.row_bytes;
+  for (int s = 0; s < c.nranks; ++s) m |= addr(c.src[s]) | addr(c.dst[s]);
+  if ((m & 15) == 0) return dispatch_impl<u32x4, P>(c, c.row_bytes / 16);
+  if ((m & 3) == 0) return dispatch_impl<uint32_t, P>(c, c.row_bytes / 4);
+  if ((m & 1) == 0) return dispatch_impl<uint16_t, P>(c, c.row_bytes / 2);
+  return dispatch_impl<uint8_t, P>(c, c.row_bytes);
+}
+
+template <int P>
+gc_status combine_any(const gci::MoeMoveCall& c) {
+  uint64_t m = c.row_bytes;
+  for (int s = 0; s < c.nranks; ++s) m |= addr(c.src[s]) | addr(c.dst[s]);
+  const bool vec = (m & 15) == 0;
+  if (c.t == GC_BF16)
+    return vec ? combine_impl<InBf16, true, P>(c, c.row_bytes / 16) : combine_impl<InBf16, false, P>(c, c.row_bytes / 2);
+  return vec ? combine_impl<InF32, true, P>(c, c.row_bytes / 16) : combine_impl<InF32, false, P>(c, c.row_bytes / 4);
+}
+
+}  // namespace
+
+namespace gci {
+
+gc_status launch_moe_route(const MoeRouteCall& c) {
+  return c.nranks <= 8 ? route_impl<8>(c) : route_impl<64>(c);
+}
+
+gc_status launch_moe_dispatch(const MoeMoveCall& c) {
+  return c.nranks <= 8 ? dispatch_any<8>(c) : dispatch_any<64>(c);
+}
+
+gc_status launch_moe_combine(const MoeMoveCall& c) {
+  return c.nranks <= 8 ? combine_any<8>(c) : combine_any<64>(c);
+}
+
+}  // namespace gci

@@ -50,6 +50,7 @@ WORKLOADS = {
                         cap_bytes=25 * 1024 * 1024),
     "fsdp_layer_n64": dict(nranks=64, dtype="bf16", grad_sigma=1e-3, param_sigma=0.02),
     "moe_a2a_n8": dict(nranks=8, tokens=16384, hidden=4096, experts=64, topk=2, zipf_s=1.1),
+    "moe_ep_n8": dict(nranks=8, tokens=16384, hidden=4096, experts=64, topk=2, zipf_s=1.1, dtype="bf16"),
 }
 
 

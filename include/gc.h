@@ -132,6 +132,82 @@ gc_status gc_all_to_all(const void* const* send, void* const* recv, const int64_
                         int nranks, int experts_per_rank, size_t row_bytes, hipStream_t stream);
 
 /*
+ * Expert-parallel MoE around the all-to-all (DTLM §8 "专家并行和 MoE 通信": the
+ * router picks top-k experts per token, tokens are packed by target expert /
+ * rank and dispatched with All-to-AllV, the local experts run, a second
+ * All-to-AllV brings the results back and the token order is restored).
+ * Ranks hold E = experts_per_rank experts each; global expert g lives on rank
+ * g / E as local expert g % E.  The router and the experts are the caller's.
+ *
+ * A route is one (token, k) pair of a source rank, numbered t * topk + k.
+ * Its destination row in rank d's receive buffer follows gc_all_to_all's
+ * receive layout: blocks by local expert, then by source, and inside a block
+ * the routes in ascending route number (the order a source sends them in,
+ * by global expert, then token).
+ */
+
+/*
+ * Scratch bytes gc_moe_route needs, nbins = nranks * E: each source's routes
+ * are cut into tiles of max(512, nbins rounded up to 64) routes, and the
+ * plan keeps one int32 per tile and global expert, plus nranks * nbins int32.
+ */
+size_t gc_moe_route_scratch_bytes(const int64_t* ntokens, int nranks, int topk, int experts_per_rank);
+
+/*
+ * Routing plan, computed on the device.
+ *   experts[s]  DEVICE int32 [ntokens[s] * topk]: global expert of each route of
+ *               source s (token-major).  Ids outside [0, nranks * E) mark a
+ *               dropped route: it is not counted and its dest entry is (-1, -1).
+ *   ntokens     HOST int64 [nranks] tokens per source (0 allowed).
+ *   splits      DEVICE int64 [nranks][nranks][E] out: routes of source s to local
+ *               expert e of rank d, the table gc_all_to_all takes (copy it to the
+ *               host to size the receive buffers).
+ *   dest[s]     DEVICE int32 pairs [ntokens[s] * topk][2] out: (rank, row) of
+ *               each route's copy in the receive buffers.
+ *   scratch     DEVICE, 256-byte aligned, at least gc_moe_route_scratch_bytes().
+ * 1 <= topk <= 8; nranks * E <= 8192; total routes below 2^31.  Output and
+ * scratch buffers must not overlap each other or the inputs.
+ */
+gc_status gc_moe_route(const int32_t* const* experts, const int64_t* ntokens, int nranks, int topk,
+                       int experts_per_rank, int64_t* splits, int32_t* const* dest, void* scratch,
+                       size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * Dispatch straight from token order: the pack by expert fused into the
+ * all-to-all.  Row t of tokens[s] is read once and copied to recv[d] row r for
+ * each of its routes (d, r) = dest[s][t * topk + k].  Equal to packing every
+ * source's routes in their send order and calling gc_all_to_all with the
+ * splits of gc_moe_route.
+ *   tokens[s]   DEVICE [ntokens[s]] rows of row_bytes bytes.
+ *   dest[s]     DEVICE int32 pairs, as gc_moe_route writes them.
+ *   recv[d]     DEVICE [recv_rows[d]] rows; recv_rows is a HOST int64 [nranks].
+ * Entries of dest outside [0, nranks) x [0, recv_rows[d]) are skipped.  Pure
+ * data movement (bit-exact); receive buffers must not overlap anything else.
+ */
+gc_status gc_moe_dispatch(const void* const* tokens, const int64_t* ntokens, const int32_t* const* dest,
+                          int nranks, int topk, size_t row_bytes, void* const* recv,
+                          const int64_t* recv_rows, hipStream_t stream);
+
+/*
+ * Combine: the inverse all-to-all fused with the weighted un-permute back to
+ * token order.  For every source s and token t,
+ *   out[s][t] = sum over k of weights[s][t * topk + k] * expert_out[d][r],
+ *   (d, r) = dest[s][t * topk + k], hidden elements of type t per row.
+ * Arithmetic: rows are widened to fp32, each product is rounded to fp32, the
+ * products are added in k order starting from k = 0, and the sum is rounded
+ * once to the row type (bf16: nearest, ties to even).  Routes whose entry lies
+ * outside the expert_out buffers are left out of the sum; a token with no
+ * route left gets zeros.
+ *   expert_out[d]  DEVICE [expert_rows[d]] rows in rank d's receive layout.
+ *   weights[s]     DEVICE fp32 [ntokens[s] * topk] gate weights.
+ *   out[s]         DEVICE [ntokens[s]] rows.
+ * t is GC_BF16 or GC_FP32.  Output buffers must not overlap anything else.
+ */
+gc_status gc_moe_combine(const void* const* expert_out, const int64_t* expert_rows, const int32_t* const* dest,
+                         const float* const* weights, const int64_t* ntokens, int nranks, int topk,
+                         size_t hidden, gc_dtype t, void* const* out, hipStream_t stream);
+
+/*
  * Bucket plan: DDP gradient buckets (AIG6 §6.2.4; NXMR §5.1) and the FSDP
  * FlatParameter layout (DTLM §4 FSDP1).
  *   Tensors are visited in reverse definition order when `reverse` is nonzero

@@ -184,3 +184,71 @@ def test_bucket_all_reduce_validation():
     assert _status(gc.gc_bucket_all_reduce, ip.handle, 0, _ptrs(2), 2, op="sum", sumsq=FAKE,
                    stream=0) == gc.GC_ERR_UNSUPPORTED
     assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, tensors, 65, stream=0) == gc.GC_ERR_UNSUPPORTED
+
+
+def test_moe_route_validation():
+    route = gc.gc_moe_route
+    nt = [100, 0, 37]
+    need = gc.gc_moe_route_scratch_bytes(nt, 2, 4)
+    # tiles of 512 routes: 1 + 0 + 1 tiles x 12 experts, then 3 x 12 offsets, each 256-aligned
+    assert need == 256 + 256
+    assert gc.gc_moe_route_scratch_bytes(nt, 9, 4) == 0                     # topk > 8
+    assert gc.gc_moe_route_scratch_bytes([1] * 64, 1, 129) == 0              # 64 * 129 experts > 8192
+    assert gc.gc_moe_route_scratch_bytes([-1, 2, 3], 1, 1) == 0
+    big = gc.gc_moe_route_scratch_bytes([10_000] * 2, 1, 4096)               # tiles of 8192 routes
+    assert big == 4 * 8192 * 4 + 2 * 8192 * 4                             # 2 tiles per source
+    ex, de = _ptrs(3), _ptrs(3, base=FAKE + (1 << 40))
+    sp, sc = FAKE + (1 << 41), FAKE + (1 << 42)
+    ok = dict(experts=ex, ntokens=nt, topk=2, experts_per_rank=4, splits=sp, dest=de, scratch=sc,
+              scratch_bytes=need, stream=0)
+    def st(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(route, **a)
+    assert st(scratch_bytes=need - 1) == gc.GC_ERR_INVALID_ARG
+    assert st(scratch=sc + 16) == gc.GC_ERR_INVALID_ARG                     # not 256-aligned
+    assert st(splits=sp + 4) == gc.GC_ERR_INVALID_ARG
+    assert st(dest=de[:2] + [de[2] + 4]) == gc.GC_ERR_INVALID_ARG           # dest must be 8-aligned
+    assert st(experts=[ex[0], ex[1], 0]) == gc.GC_ERR_INVALID_ARG           # null with tokens
+    assert st(topk=0) == gc.GC_ERR_INVALID_ARG
+    assert st(topk=9) == gc.GC_ERR_UNSUPPORTED
+    assert st(scratch=de[0] + 512) == gc.GC_ERR_INVALID_ARG                 # scratch overlaps a dest table
+    assert st(splits=ex[2]) == gc.GC_ERR_INVALID_ARG                        # an output over an input
+    assert st(ntokens=[100, -1, 37]) == gc.GC_ERR_INVALID_ARG
+    assert st(ntokens=[1 << 30, 1 << 30, 0]) == gc.GC_ERR_UNSUPPORTED       # 2^31 routes
+
+
+def test_moe_dispatch_combine_validation():
+    nt, rows = [10, 0, 3], [8, 20, 0]
+    tok, de = _ptrs(3), _ptrs(3, base=FAKE + (1 << 40))
+    rv, w = _ptrs(3, base=FAKE + (1 << 41)), _ptrs(3, base=FAKE + (1 << 42))
+    disp = dict(tokens=tok, ntokens=nt, dest=de, topk=2, row_bytes=64, recv=rv, recv_rows=rows, stream=0)
+    def sd(**kw):
+        a = dict(disp)
+        a.update(kw)
+        return _status(gc.gc_moe_dispatch, **a)
+    assert sd(row_bytes=0) == gc.GC_ERR_INVALID_ARG
+    assert sd(topk=9) == gc.GC_ERR_UNSUPPORTED
+    assert sd(recv=[rv[0], rv[0] + 64, rv[2]]) == gc.GC_ERR_INVALID_ARG     # receive buffers overlap
+    assert sd(recv=[tok[0] + 64] + rv[1:]) == gc.GC_ERR_INVALID_ARG         # receive over the tokens
+    assert sd(recv=[de[0]] + rv[1:]) == gc.GC_ERR_INVALID_ARG               # receive over a dest table
+    assert sd(dest=[de[0] + 4] + de[1:]) == gc.GC_ERR_INVALID_ARG
+    assert sd(recv=[rv[0], 0, rv[2]]) == gc.GC_ERR_INVALID_ARG              # null with rows
+    assert sd(recv_rows=[8, -1, 0]) == gc.GC_ERR_INVALID_ARG
+    assert sd(ntokens=[0, 0, 0], recv_rows=[0, 0, 0]) == gc.GC_OK          # nothing to do
+    comb = dict(expert_out=rv, expert_rows=rows, dest=de, weights=w, ntokens=nt, topk=2, hidden=32,
+                dtype="bf16", out=tok, stream=0)
+    def sc(**kw):
+        a = dict(comb)
+        a.update(kw)
+        return _status(gc.gc_moe_combine, **a)
+    assert sc(dtype="int32") == gc.GC_ERR_UNSUPPORTED
+    assert sc(dtype=7) == gc.GC_ERR_INVALID_ARG
+    assert sc(hidden=0) == gc.GC_ERR_INVALID_ARG
+    assert sc(weights=None) == gc.GC_ERR_INVALID_ARG
+    assert sc(weights=[w[0] + 2] + w[1:]) == gc.GC_ERR_INVALID_ARG          # misaligned weights
+    assert sc(out=[tok[0], tok[1], tok[0] + 128]) == gc.GC_ERR_INVALID_ARG  # 10 rows of 64 B overlap
+    assert sc(out=[w[0]] + tok[1:]) == gc.GC_ERR_INVALID_ARG                # output over the weights
+    assert sc(out=[rv[1] + 64] + tok[1:]) == gc.GC_ERR_INVALID_ARG          # output over expert rows
+    assert sc(dtype="fp32", out=[tok[0] + 2] + tok[1:]) == gc.GC_ERR_INVALID_ARG
+    assert sc(ntokens=[0, 0, 0]) == gc.GC_OK

@@ -258,3 +258,58 @@ def test_moe_a2a_n8_full():
         assert np.array_equal(got, want), f"rank {d} sampled rows"
     # the skew the workload is meant to have: most rows land on rank 0
     assert 0.55 < recv_rows[0] / recv_rows.sum() < 0.67
+
+
+def test_moe_ep_n8_full():
+    """Routing plan, dispatch and combine at full size, in bench.py's layout.
+    The plan is compared with the oracle's for all 262,144 routes; dispatched
+    and combined rows are sampled against values the oracle computes from the
+    host generator (identity experts: a token's K expert rows are its own row)."""
+    from gen.workloads import route_tokens
+    from oracle import moe as OM
+    cfg = WORKLOADS["moe_ep_n8"]
+    N, T, H, K = cfg["nranks"], cfg["tokens"], cfg["hidden"], cfg["topk"]
+    E = cfg["experts"] // N
+    experts = [route_tokens(SEED, s, T, cfg["experts"], K, cfg["zipf_s"]) for s in range(N)]
+    want_splits, dr, dw = OM.route_plan(experts, N, E)
+    arena = gc.RankArena(N)
+    tokens = arena.alloc(T * H, "bf16")
+    for s in range(N):
+        GD.fill_normal_bf16(tokens[s], G.stream_key(SEED, s, 0), 1.0)
+    weights = [torch.empty(T * K, dtype=torch.float32, device=DEV) for _ in range(N)]
+    for s in range(N):
+        GD.fill_uniform_f32(weights[s], G.stream_key(SEED, s, 3))
+    ex_dev = [torch.from_numpy(e.reshape(-1).astype(np.int32)).to(DEV) for e in experts]
+    splits = torch.empty(N * N * E, dtype=torch.int64, device=DEV)
+    dest = [torch.empty(T * K * 2, dtype=torch.int32, device=DEV) for _ in range(N)]
+    scratch = torch.empty(gc.gc_moe_route_scratch_bytes([T] * N, K, E), dtype=torch.uint8, device=DEV)
+    gc.gc_moe_route(ex_dev, [T] * N, K, E, splits, dest, scratch)
+    torch.cuda.synchronize()
+    assert np.array_equal(splits.cpu().numpy().reshape(N, N, E), want_splits)
+    for s in range(N):
+        got = dest[s].cpu().numpy().reshape(-1, 2)
+        assert np.array_equal(got[:, 0], dr[s]) and np.array_equal(got[:, 1], dw[s]), f"source {s}"
+    rows = [int(x) for x in want_splits.sum(axis=(0, 2))]
+    recv_full = arena.alloc(max(rows) * H, "bf16")
+    recv = [recv_full[d][:rows[d] * H] for d in range(N)]
+    for r in recv:
+        r.view(torch.int16).fill_(-1)                      # 0xFFFF, a NaN pattern no token row holds whole
+    gc.gc_moe_dispatch(tokens, [T] * N, dest, K, H * 2, recv, rows)
+    out = arena.alloc(T * H, "bf16")
+    gc.gc_moe_combine(recv, rows, dest, weights, [T] * N, K, H, "bf16", out)
+    torch.cuda.synchronize()
+    for d in range(N):                                  # every receive row was written
+        unwritten = (recv[d].view(-1, H).view(torch.int16) == -1).all(dim=1).sum().item()
+        assert unwritten == 0, f"rank {d}: {unwritten} rows not written"
+    rng = np.random.default_rng(11)
+    for s in (0, 5, 7):
+        pick = np.unique(np.concatenate([rng.integers(0, T, size=96), [0, T - 1]]))
+        tok_rows = np.stack([G.normal_bf16(G.stream_key(SEED, s, 0), int(t) * H + np.arange(H), 1.0) for t in pick])
+        for k in range(K):                              # dispatched copies
+            d, r = dr[s][pick * K + k], dw[s][pick * K + k]
+            got = np.stack([from_dev(recv[int(dd)].view(-1, H)[int(rr)]) for dd, rr in zip(d, r)])
+            assert np.array_equal(got, tok_rows), f"source {s} k {k}"
+        w = G.uniform_f32(G.stream_key(SEED, s, 3), np.arange(T * K, dtype=np.uint64)).reshape(T, K)[pick]
+        want = OM.combine_rows(np.stack([tok_rows] * K), w, "bf16")
+        got = from_dev(out[s].view(-1, H).index_select(0, torch.from_numpy(pick).to(DEV)))
+        assert_same(got.reshape(-1), want.reshape(-1), "bf16", f"source {s} combine")
