@@ -18,7 +18,8 @@ fsdp_layer_n64, moe_a2a_n8 (the remaining parity configurations, measured the
 same way; the zero-copy DDP step all-reduces each bucket in place over the
 gradient tensors instead of packing and unpacking it), and moe_ep_n8 (the
 expert-parallel MoE data flow: routing plan, dispatch from token order and
-weighted combine back to token order, identity experts).
+weighted combine back to token order, identity experts), and fsdp2_layer_n64
+(the FSDP layer sharded per parameter on dim 0, as FSDP2 does).
 """
 
 import argparse
@@ -45,7 +46,7 @@ KERNEL_SOURCES = {
 }
 WORKLOAD_KERNELS = {"ar_bf16_n8": "reduce", "ar_fp32_n4": "reduce", "ddp_llama7b": "reduce",
                     "fsdp_layer_n64": "reduce", "ddp_llama7b_zero_copy": "bucket", "moe_a2a_n8": "a2a",
-                    "moe_ep_n8": "moe"}
+                    "moe_ep_n8": "moe", "fsdp2_layer_n64": "reduce"}
 
 
 def parse():
@@ -55,7 +56,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ar_bf16_n8",
                    choices=["ar_bf16_n8", "ar_fp32_n4", "ddp_llama7b", "ddp_llama7b_zero_copy", "fsdp_layer_n64",
-                            "moe_a2a_n8", "moe_ep_n8"])
+                            "moe_a2a_n8", "moe_ep_n8", "fsdp2_layer_n64"])
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--layout", default="arena", choices=["arena", "staggered", "separate"],
                    help="placement of the rank buffers in HBM")
@@ -351,6 +352,92 @@ class FsdpWorkload(Workload):
         return run, self.N * m * 2 + m * 4, f"oracle reduce-scatter of {m} outputs of owner 5 (64-way fold each)"
 
 
+class Fsdp2Workload(Workload):
+    """The same layer as FSDP2 shards it, 64 ranks: every parameter its own dim-0 shard (DTensor Shard(0)),
+    reduce-scatter (avg) bf16 -> fp32 and all-gather bf16 per parameter, one launch each."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+        import collective_communication_reduction_amd as gc
+        from gen import device as GD
+        from gen.workloads import fsdp_layer_shapes
+        self.gc = gc
+        self.N = N = 64
+        self.name = "fsdp2_layer_n64"
+        shapes = fsdp_layer_shapes()
+        self.rows = [r for _, r, _ in shapes]
+        self.cols = [c for _, _, c in shapes]
+        P = len(shapes)
+        numel = [r * c for r, c in zip(self.rows, self.cols)]
+        offs = np.concatenate([[0], np.cumsum(numel)]).astype(np.int64)
+        S = int(offs[-1])
+
+        def shard(p, r):
+            c = -(-self.rows[p] // N)
+            return min(self.rows[p], r * c) * self.cols[p], min(self.rows[p], (r + 1) * c) * self.cols[p]
+        soffs = [np.concatenate([[0], np.cumsum([shard(p, r)[1] - shard(p, r)[0] for p in range(P)])]).astype(np.int64)
+                 for r in range(N)]
+        most = max(int(x[-1]) for x in soffs)
+        L = Layout(args, N)
+        self.layout = L.name()
+        grads = L.buffers(S, torch.bfloat16)
+        gsh = L.buffers(most, torch.float32)
+        psh = L.buffers(most, torch.bfloat16)
+        params = L.buffers(S, torch.bfloat16)
+        for r in range(N):
+            GD.fill_normal_bf16(grads[r], _keyed(args.seed, r, 0), 1e-3)
+            GD.fill_normal_bf16(psh[r], _keyed(args.seed, r, 1), 0.02)
+        self.bufs = (grads, gsh, psh, params)
+
+        def views(buf, o, r):
+            return [buf[r][o[r][p] if isinstance(o, list) else o[p]:(o[r][p + 1] if isinstance(o, list) else o[p + 1])]
+                    for p in range(P)]
+        # the gradient, shard and parameter tensors persist across steps: marshal once
+        self.g = gc.gc_pointers([t for r in range(N) for t in views(grads, offs, r)])
+        self.gs = gc.gc_pointers([t for r in range(N) for t in views(gsh, soffs, r)])
+        self.ps = gc.gc_pointers([t for r in range(N) for t in views(psh, soffs, r)])
+        self.pa = gc.gc_pointers([t for r in range(N) for t in views(params, offs, r)])
+        shard_elems = sum(int(x[-1]) for x in soffs)
+        self.rs_bytes = N * S * 2 + shard_elems * 4
+        self.ag_bytes = shard_elems * 2 + N * S * 2
+        self.bytes_per_step = self.rs_bytes + self.ag_bytes
+        self.S = S
+        self.dominant = "reduce_vec_kernel (per-parameter reduce-scatter, 64 ranks; 9 launches)"
+        self.dominant_bytes = self.rs_bytes
+        torch.cuda.synchronize()
+
+    def rs(self):
+        self.gc.gc_fsdp2_reduce_scatter(self.g, self.gs, self.rows, self.cols, self.N, "bf16", "fp32", "avg", "ring")
+
+    def step(self, k):
+        self.rs()
+        self.gc.gc_fsdp2_all_gather(self.ps, self.pa, self.rows, self.cols, self.N, "bf16")
+
+    def dominant_launch(self, k):
+        self.rs()
+
+    def config(self):
+        return {"workload": self.name, "nranks": self.N, "params": len(self.rows), "numel": self.S,
+                "sharding": "per-parameter dim 0 (torch.chunk rule)", "rs": "bf16->fp32 avg ring", "ag": "bf16",
+                "layout": self.layout}
+
+    def cpu_sample(self, seed):
+        import numpy as np
+        from gen import host as G
+        from oracle import fsdp2 as F2
+        # q_proj and the two norm vectors, 64 ranks
+        rows, cols = [4096, 4096, 4096], [4096, 1, 1]
+        n = [r * c for r, c in zip(rows, cols)]
+        grads = [[G.normal_bf16(_keyed(seed, r, 0), np.arange(k, dtype=np.uint64) + 1000 * p, 1e-3)
+                  for p, k in enumerate(n)] for r in range(self.N)]
+
+        def run():
+            return F2.reduce_scatter(grads, rows, cols, "bf16", "fp32", "avg", "ring")
+        nbytes = self.N * sum(n) * 2 + sum(n) * 4
+        return run, nbytes, "oracle per-parameter ring reduce-scatter of 64 ranks x (q_proj 4096x4096 + 2 x 4096) bf16"
+
+
 class MoeWorkload(Workload):
     """MoE dispatch all-to-all, 8 ranks x 16384 tokens x 4096 bf16, top-2 of 64 experts, Zipf(1.1)."""
 
@@ -527,6 +614,8 @@ def make(args):
         return FsdpWorkload(args)
     if args.workload == "moe_ep_n8":
         return MoeEpWorkload(args)
+    if args.workload == "fsdp2_layer_n64":
+        return Fsdp2Workload(args)
     return MoeWorkload(args)
 
 

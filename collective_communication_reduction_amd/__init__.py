@@ -72,6 +72,9 @@ _c_ar_scratch = _sig("gc_all_reduce_scratch_bytes", _sz, _sz, _int, _int, _int)
 _c_ar = _sig("gc_all_reduce", _int, _VPP, _VPP, _sz, _int, _int, _int, _int, _int, _vp, _sz, _vp)
 _c_a2a = _sig("gc_all_to_all", _int, _VPP, _VPP, ctypes.POINTER(ctypes.c_int64), _int, _int, _sz, _vp)
 _I64P = ctypes.POINTER(ctypes.c_int64)
+_SZP = ctypes.POINTER(ctypes.c_size_t)
+_c_fsdp2_rs = _sig("gc_fsdp2_reduce_scatter", _int, _VPP, _VPP, _SZP, _SZP, _int, _int, _int, _int, _int, _int, _vp)
+_c_fsdp2_ag = _sig("gc_fsdp2_all_gather", _int, _VPP, _VPP, _SZP, _SZP, _int, _int, _int, _vp)
 _c_moe_scratch = _sig("gc_moe_route_scratch_bytes", _sz, _I64P, _int, _int, _int)
 _c_moe_route = _sig("gc_moe_route", _int, _VPP, _I64P, _int, _int, _int, _vp, _VPP, _vp, _sz, _vp)
 _c_moe_dispatch = _sig("gc_moe_dispatch", _int, _VPP, _I64P, _VPP, _int, _int, _sz, _VPP, _I64P, _vp)
@@ -245,6 +248,51 @@ def gc_all_to_all(send, recv, splits, row_bytes, stream=None):
     _check(_c_a2a(_ptr_array(send), _ptr_array(recv), sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, e,
                   int(row_bytes), _stream(stream, _first(send))), "gc_all_to_all")
     return recv
+
+
+def _sz_array(xs):
+    xs = [int(x) for x in xs]
+    return (ctypes.c_size_t * max(1, len(xs)))(*xs)
+
+
+def _rank_major(xs, nranks, nparams):
+    """Accept [rank][param] nested lists, a flat rank-major list, or a marshalled array."""
+    if isinstance(xs, ctypes.Array):
+        return xs
+    if len(xs) == nranks and nparams and isinstance(xs[0], (list, tuple)):
+        xs = [x for row in xs for x in row]
+    if len(xs) != nranks * nparams:
+        raise ValueError("need nranks * nparams pointers")
+    return _ptr_array(xs)
+
+
+def gc_fsdp2_reduce_scatter(grads, shards, rows, cols, nranks, in_dtype, out_dtype=None, op="avg", order="ring",
+                            stream=None):
+    """Per-parameter Shard(0) reduce-scatter; grads / shards as [rank][param] (or flat rank-major)."""
+    P = len(rows)
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    g = _rank_major(grads, nranks, P)
+    sh = _rank_major(shards, nranks, P)
+    like = None if isinstance(grads, ctypes.Array) else _first([x for row in grads for x in row]
+                                                                if grads and isinstance(grads[0], (list, tuple))
+                                                                else grads)
+    _check(_c_fsdp2_rs(g, sh, _sz_array(rows), _sz_array(cols), P, int(nranks), _dtype_code(in_dtype),
+                       _dtype_code(out_dtype), _enum(_OP, op), _enum(_ORDER, order), _stream(stream, like)),
+           "gc_fsdp2_reduce_scatter")
+    return shards
+
+
+def gc_fsdp2_all_gather(shards, params, rows, cols, nranks, dtype, stream=None):
+    """Per-parameter Shard(0) all-gather; shards / params as [rank][param] (or flat rank-major)."""
+    P = len(rows)
+    sh = _rank_major(shards, nranks, P)
+    pa = _rank_major(params, nranks, P)
+    like = None if isinstance(params, ctypes.Array) else _first([x for row in params for x in row]
+                                                                 if params and isinstance(params[0], (list, tuple))
+                                                                 else params)
+    _check(_c_fsdp2_ag(sh, pa, _sz_array(rows), _sz_array(cols), P, int(nranks), _dtype_code(dtype),
+                       _stream(stream, like)), "gc_fsdp2_all_gather")
+    return params
 
 
 def _i64_array(xs):

@@ -280,6 +280,137 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
   return GC_OK;
 }
 
+// ------------------------------------------------------------- FSDP2 Shard(0)
+
+namespace {
+
+// Rows of rank r's dim-0 shard of a parameter with `rows` rows (torch.chunk rule).
+struct RowShard {
+  uint64_t lo, hi;
+};
+
+RowShard row_shard(uint64_t rows, int nranks, int r) {
+  const uint64_t c = (rows + nranks - 1) / nranks;
+  return RowShard{std::min<uint64_t>(rows, r * c), std::min<uint64_t>(rows, (r + 1) * c)};
+}
+
+// A buffer of parameter p on rank r; `in_place` marks an output that may hold
+// the same (p, r) input inside it (or sit inside it) at the shard's offset.
+struct Tagged {
+  Span s;
+  int p, r;
+  bool in_place;
+};
+
+// True if two outputs overlap, or an output overlaps an input other than its
+// own in-place partner.  Outputs are sorted once; each input is matched
+// against the outputs it can reach by binary search.
+bool tagged_conflict(const std::vector<Tagged>& outs, const std::vector<Tagged>& ins) {
+  std::vector<Span> os;
+  std::vector<Tagged> sorted;
+  for (const Tagged& o : outs) {
+    os.push_back(o.s);
+    if (!o.s.empty()) sorted.push_back(o);
+  }
+  if (any_overlap(os)) return true;
+  std::sort(sorted.begin(), sorted.end(), [](const Tagged& a, const Tagged& b) { return a.s.lo < b.s.lo; });
+  for (const Tagged& i : ins) {
+    if (i.s.empty()) continue;
+    // Disjoint outputs sorted by start are sorted by end too: skip those ending at or before i.lo.
+    auto it = std::partition_point(sorted.begin(), sorted.end(), [&](const Tagged& o) { return o.s.hi <= i.s.lo; });
+    for (; it != sorted.end() && it->s.lo < i.s.hi; ++it) {
+      if (it->in_place && it->p == i.p && it->r == i.r) continue;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Shared checks of the per-parameter calls.  full[r * P + p] holds rows[p] *
+// cols[p] elements of es_full bytes, part[r * P + p] rank r's shard of es_part
+// bytes (NULL allowed when empty).  `outputs_are_parts` picks which side is
+// written; with `in_place_ok` a shard may sit exactly at its offset inside
+// the same rank's full buffer.
+gc_status fsdp2_check(const void* const* full, const void* const* part, const size_t* rows, const size_t* cols,
+                      int P, int N, size_t es_full, size_t es_part, bool outputs_are_parts, bool in_place_ok) {
+  GC_TRY(check_ranks(N));
+  if (!full || !part || !rows || !cols || P < 0) return GC_ERR_INVALID_ARG;
+  std::vector<Tagged> outs, ins;
+  for (int p = 0; p < P; ++p) {
+    if (mul_overflows(rows[p], cols[p]) || mul_overflows(rows[p] * cols[p], 4)) return GC_ERR_INVALID_ARG;
+    const uint64_t S = rows[p] * cols[p];
+    if (S == 0) continue;
+    for (int r = 0; r < N; ++r) {
+      const void* f = full[static_cast<size_t>(r) * P + p];
+      const void* q = part[static_cast<size_t>(r) * P + p];
+      const RowShard sh = row_shard(rows[p], N, r);
+      const uint64_t n = (sh.hi - sh.lo) * cols[p];
+      if (!f || addr(f) % es_full) return GC_ERR_INVALID_ARG;
+      if (n && (!q || addr(q) % es_part)) return GC_ERR_INVALID_ARG;
+      const bool in_place = in_place_ok && n && addr(q) == addr(f) + sh.lo * cols[p] * es_full;
+      const Tagged ft{span(f, S * es_full), p, r, in_place};
+      const Tagged qt{span(n ? q : nullptr, n * es_part), p, r, in_place};
+      (outputs_are_parts ? outs : ins).push_back(qt);
+      (outputs_are_parts ? ins : outs).push_back(ft);
+    }
+  }
+  return tagged_conflict(outs, ins) ? GC_ERR_INVALID_ARG : GC_OK;
+}
+
+}  // namespace
+
+extern "C" gc_status gc_fsdp2_reduce_scatter(const void* const* grads, void* const* shards, const size_t* rows,
+                                             const size_t* cols, int nparams, int nranks, gc_dtype in_t,
+                                             gc_dtype out_t, gc_op op, gc_order order, hipStream_t stream) {
+  GC_TRY(check_ranks(nranks));
+  if (!valid_dtype(in_t) || !valid_dtype(out_t) || !valid_op(op) || !valid_order(order)) return GC_ERR_INVALID_ARG;
+  if ((in_t == GC_INT32) != (out_t == GC_INT32)) return GC_ERR_UNSUPPORTED;
+  if (op == GC_AVG && in_t == GC_INT32) return GC_ERR_UNSUPPORTED;
+  const size_t ei = elem_bytes(in_t), eo = elem_bytes(out_t);
+  GC_TRY(fsdp2_check(grads, const_cast<const void* const*>(shards), rows, cols, nparams, nranks, ei, eo, true,
+                     in_t == out_t));
+  const int N = nranks, P = nparams;
+  std::vector<const void*> in(N);
+  std::vector<void*> out(N);
+  for (int p = 0; p < P; ++p) {
+    const uint64_t S = rows[p] * cols[p];
+    if (S == 0) continue;
+    for (int r = 0; r < N; ++r) {
+      in[r] = grads[r * P + p];
+      out[r] = shards[r * P + p];
+    }
+    const uint64_t c = (rows[p] + N - 1) / N * cols[p];
+    gci::ReduceCall call{in.data(), out.data(), N, S, c, in_t, out_t, op == GC_AVG, order == GC_ORDER_RING, stream};
+    GC_TRY(gci::launch_reduce_scatter(call));
+  }
+  return GC_OK;
+}
+
+extern "C" gc_status gc_fsdp2_all_gather(const void* const* shards, void* const* params, const size_t* rows,
+                                         const size_t* cols, int nparams, int nranks, gc_dtype t,
+                                         hipStream_t stream) {
+  GC_TRY(check_ranks(nranks));
+  if (!valid_dtype(t)) return GC_ERR_INVALID_ARG;
+  const size_t es = elem_bytes(t);
+  GC_TRY(fsdp2_check(const_cast<const void* const*>(params), shards, rows, cols, nparams, nranks, es, es, false,
+                     true));
+  const int N = nranks, P = nparams;
+  std::vector<const void*> in(N);
+  std::vector<void*> out(N);
+  for (int p = 0; p < P; ++p) {
+    const uint64_t S = rows[p] * cols[p];
+    if (S == 0) continue;
+    for (int r = 0; r < N; ++r) {
+      in[r] = shards[r * P + p];
+      out[r] = params[r * P + p];
+    }
+    const uint64_t c = (rows[p] + N - 1) / N * cols[p];
+    gci::ReduceCall call{in.data(), out.data(), N, S, c, t, t, false, false, stream};
+    GC_TRY(gci::launch_all_gather(call));
+  }
+  return GC_OK;
+}
+
 // ------------------------------------------------------------------------ MoE
 
 namespace {

@@ -390,6 +390,7 @@ gc_status run_reduce(const gci::ReduceCall& c) {
     const uint64_t wb = std::min<uint64_t>(16, Out::vec_bytes(VE));
     for (int j = 0; j < N && vec; ++j) {
       const uint64_t lo = std::min<uint64_t>(c.S, static_cast<uint64_t>(j) * c.c);
+      if (lo == std::min<uint64_t>(c.S, lo + c.c)) continue;  // empty chunk: its output is never touched
       const uint64_t vlo = lo <= static_cast<uint64_t>(ph) ? 0 : (lo - ph + VE - 1) / VE;
       const uint64_t first = ph + vlo * VE;
       if (((addr(c.out[j]) + (first - lo) * Out::ES) % wb) != 0) vec = false;
@@ -426,6 +427,7 @@ gc_status run_gather(const gci::ReduceCall& c) {
   bool vec = ph >= 0;
   for (int j = 0; j < N && vec; ++j) {
     const uint64_t lo = std::min<uint64_t>(c.S, static_cast<uint64_t>(j) * c.c);
+    if (lo == std::min<uint64_t>(c.S, lo + c.c)) continue;  // empty shard: never read
     const uint64_t vlo = lo <= static_cast<uint64_t>(ph) ? 0 : (lo - ph + VE - 1) / VE;
     const uint64_t first = ph + vlo * VE;
     if (((addr(c.in[j]) + (first - lo) * ES) & 15) != 0) vec = false;

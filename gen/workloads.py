@@ -43,12 +43,21 @@ def fsdp_layer_tensors():
     return list(LAYER_TENSORS)
 
 
+def fsdp_layer_shapes():
+    """(name, rows, cols) of the layer's parameters: Linear weights are [out, in], norms [hidden] (one column)."""
+    shapes = {"q_proj": (HIDDEN, HIDDEN), "k_proj": (HIDDEN, HIDDEN), "v_proj": (HIDDEN, HIDDEN),
+              "o_proj": (HIDDEN, HIDDEN), "gate_proj": (MLP, HIDDEN), "up_proj": (MLP, HIDDEN),
+              "down_proj": (HIDDEN, MLP), "attn_norm": (HIDDEN, 1), "mlp_norm": (HIDDEN, 1)}
+    return [(n, *shapes[n]) for n, _ in LAYER_TENSORS]
+
+
 WORKLOADS = {
     "ar_fp32_n4": dict(nranks=4, count=1_048_576, dtype="fp32", op="sum", dist="uniform"),
     "ar_bf16_n8": dict(nranks=8, count=33_554_432, dtype="bf16", op="avg", dist="normal", sigma=1e-3),
     "ddp_llama7b": dict(nranks=8, dtype="bf16", op="avg", dist="normal", sigma=1e-3,
                         cap_bytes=25 * 1024 * 1024),
     "fsdp_layer_n64": dict(nranks=64, dtype="bf16", grad_sigma=1e-3, param_sigma=0.02),
+    "fsdp2_layer_n64": dict(nranks=64, dtype="bf16", grad_sigma=1e-3, param_sigma=0.02),
     "moe_a2a_n8": dict(nranks=8, tokens=16384, hidden=4096, experts=64, topk=2, zipf_s=1.1),
     "moe_ep_n8": dict(nranks=8, tokens=16384, hidden=4096, experts=64, topk=2, zipf_s=1.1, dtype="bf16"),
 }
@@ -114,5 +123,5 @@ def moe_send_layout(seed, nranks, tokens, n_experts, topk, s):
     return splits, rows
 
 
-__all__ = ["WORKLOADS", "llama7b_tensors", "fsdp_layer_tensors", "zipf_cdf", "route_tokens",
+__all__ = ["WORKLOADS", "llama7b_tensors", "fsdp_layer_tensors", "fsdp_layer_shapes", "zipf_cdf", "route_tokens",
            "moe_send_layout", "stream_key", "mix64", "MASK64"]

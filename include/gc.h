@@ -132,6 +132,33 @@ gc_status gc_all_to_all(const void* const* send, void* const* recv, const int64_
                         int nranks, int experts_per_rank, size_t row_bytes, hipStream_t stream);
 
 /*
+ * FSDP2 per-parameter Shard(0) (DTLM §4 "FSDP2: DTensor / DeviceMesh"): each of
+ * nparams parameters, rows[p] x cols[p] elements stored row-major, is its own
+ * sharded tensor.  Rank r's shard of parameter p is rows [min(R, r*c),
+ * min(R, (r+1)*c)), R = rows[p], c = ceil(R / nranks), stored contiguously:
+ * the torch.chunk rule, so trailing ranks may hold fewer rows or none.
+ * Pointer arrays are HOST arrays of nranks * nparams device pointers, rank-major
+ * (entry r * nparams + p); a shard pointer may be NULL when its shard is empty.
+ *
+ * gc_fsdp2_reduce_scatter: grads[r*nparams + p] is rank r's full gradient of p;
+ *   shards[j*nparams + p] receives rank j's rows of the reduction over ranks.
+ *   Types, op and order as gc_reduce_scatter, with each parameter's row
+ *   shards as the owner chunks (ring order folds shard j from rank j+1 around
+ *   to rank j).  A shard may sit in place at its offset in the same rank's
+ *   gradient when in_t == out_t; no other overlap is allowed.
+ * gc_fsdp2_all_gather: params[d*nparams + p] receives the full parameter p on
+ *   every rank d, assembled from the shards by offset (bit-exact).  A shard
+ *   may sit in place at its offset in the same rank's parameter buffer.
+ * One launch per non-empty parameter.
+ */
+gc_status gc_fsdp2_reduce_scatter(const void* const* grads, void* const* shards, const size_t* rows,
+                                  const size_t* cols, int nparams, int nranks, gc_dtype in_t, gc_dtype out_t,
+                                  gc_op op, gc_order order, hipStream_t stream);
+
+gc_status gc_fsdp2_all_gather(const void* const* shards, void* const* params, const size_t* rows,
+                              const size_t* cols, int nparams, int nranks, gc_dtype t, hipStream_t stream);
+
+/*
  * Expert-parallel MoE around the all-to-all (DTLM §8 "专家并行和 MoE 通信": the
  * router picks top-k experts per token, tokens are packed by target expert /
  * rank and dispatched with All-to-AllV, the local experts run, a second

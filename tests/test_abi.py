@@ -252,3 +252,44 @@ def test_moe_dispatch_combine_validation():
     assert sc(out=[rv[1] + 64] + tok[1:]) == gc.GC_ERR_INVALID_ARG          # output over expert rows
     assert sc(dtype="fp32", out=[tok[0] + 2] + tok[1:]) == gc.GC_ERR_INVALID_ARG
     assert sc(ntokens=[0, 0, 0]) == gc.GC_OK
+
+
+def test_fsdp2_validation():
+    rs, ag = gc.gc_fsdp2_reduce_scatter, gc.gc_fsdp2_all_gather
+    N, rows, cols = 4, [3, 2], [5, 2]                   # shards of rows: [1,1,1,0] and [1,1,0,0]
+    G_ = [[FAKE + (r * 2 + p) * (1 << 30) for p in range(2)] for r in range(N)]
+    S_ = [[FAKE + (1 << 40) + (r * 2 + p) * (1 << 30) for p in range(2)] for r in range(N)]
+    kw = dict(rows=rows, cols=cols, nranks=N, in_dtype="bf16", out_dtype="fp32", op="avg", stream=0)
+    assert _status(rs, G_, S_, **dict(kw, in_dtype="int32", out_dtype="int32")) == gc.GC_ERR_UNSUPPORTED
+    assert _status(rs, G_, S_, **dict(kw, in_dtype="int32")) == gc.GC_ERR_UNSUPPORTED
+    assert _status(rs, G_, S_, **dict(kw, order=5)) == gc.GC_ERR_INVALID_ARG
+    bad = [row[:] for row in G_]
+    bad[1][0] = 0
+    assert _status(rs, bad, S_, **kw) == gc.GC_ERR_INVALID_ARG                 # a null gradient
+    bad = [row[:] for row in S_]
+    bad[0][1] = 0
+    assert _status(rs, G_, bad, **kw) == gc.GC_ERR_INVALID_ARG                 # a null non-empty shard
+    bad = [row[:] for row in S_]
+    bad[2][1] = bad[3][1] = 0                                                  # empty shards may be null ...
+    bad[0][0] = S_[1][0] + 8                                                   # ... but shards may not overlap
+    assert _status(rs, G_, bad, **kw) == gc.GC_ERR_INVALID_ARG
+    bad = [row[:] for row in S_]
+    bad[0][0] = G_[1][0]                                                       # a shard over another rank's gradient
+    assert _status(rs, G_, bad, **kw) == gc.GC_ERR_INVALID_ARG
+    bad = [row[:] for row in S_]
+    bad[1][0] = G_[1][0] + 2                                                   # not the in-place offset (5 elements)
+    assert _status(rs, G_, bad, **dict(kw, out_dtype="bf16")) == gc.GC_ERR_INVALID_ARG
+    bad = [row[:] for row in S_]
+    bad[1][0] = S_[1][0] + 2                                                   # misaligned fp32 shard
+    assert _status(rs, G_, bad, **kw) == gc.GC_ERR_INVALID_ARG
+    assert _status(rs, G_, S_, rows=[0, 3], cols=[7, 0], nranks=N, in_dtype="bf16", stream=0) == gc.GC_OK
+    # all-gather: params may not overlap each other or a shard, except the in-place slot
+    P_ = [[FAKE + (1 << 41) + (r * 2 + p) * (1 << 30) for p in range(2)] for r in range(N)]
+    akw = dict(rows=rows, cols=cols, nranks=N, dtype="bf16", stream=0)
+    bad = [row[:] for row in P_]
+    bad[3][1] = P_[2][1] + 4
+    assert _status(ag, S_, bad, **akw) == gc.GC_ERR_INVALID_ARG
+    bad = [row[:] for row in S_]
+    bad[2][0] = P_[1][0]
+    assert _status(ag, bad, P_, **akw) == gc.GC_ERR_INVALID_ARG
+    assert _status(ag, S_, P_, **dict(akw, dtype=9)) == gc.GC_ERR_INVALID_ARG

@@ -313,3 +313,70 @@ def test_moe_ep_n8_full():
         want = OM.combine_rows(np.stack([tok_rows] * K), w, "bf16")
         got = from_dev(out[s].view(-1, H).index_select(0, torch.from_numpy(pick).to(DEV)))
         assert_same(got.reshape(-1), want.reshape(-1), "bf16", f"source {s} combine")
+
+
+def _fsdp2_layout(N):
+    """Per-parameter shapes, offsets in a rank's flat buffer, and each rank's shard offsets."""
+    from gen.workloads import fsdp_layer_shapes
+    from oracle import fsdp2 as F2
+    shapes = fsdp_layer_shapes()
+    rows = [r for _, r, _ in shapes]
+    cols = [c for _, _, c in shapes]
+    offs = np.concatenate([[0], np.cumsum([r * c for r, c in zip(rows, cols)])]).astype(np.int64)
+    sh = [[F2.shard_elems(rows[p], cols[p], N)[r] for p in range(len(rows))] for r in range(N)]
+    soffs = [np.concatenate([[0], np.cumsum([hi - lo for lo, hi in sh[r]])]).astype(np.int64) for r in range(N)]
+    return rows, cols, offs, sh, soffs
+
+
+@pytest.mark.parametrize("N", [64, 48])
+def test_fsdp2_layer_full(N):
+    """FSDP2 per-parameter reduce-scatter (avg, bf16 -> fp32) and all-gather of
+    one transformer layer at full size, 64 ranks (every dim divides) and 48
+    ranks (uneven shards: 4096 / 48 and 11008 / 48 leave short last shards)."""
+    rows, cols, offs, sh, soffs = _fsdp2_layout(N)
+    P, S = len(rows), int(offs[-1])
+    arena = gc.RankArena(N)
+    grads = arena.alloc(S, "bf16")
+    gkeys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    pkeys = [G.stream_key(SEED, r, 1) for r in range(N)]
+    for r in range(N):
+        GD.fill_normal_bf16(grads[r], gkeys[r], 1e-3)
+    most = max(int(s[-1]) for s in soffs)
+    gsh = arena.alloc(most, "fp32")
+    gviews = [[grads[r][offs[p]:offs[p + 1]] for p in range(P)] for r in range(N)]
+    sviews = [[gsh[r][soffs[r][p]:soffs[r][p + 1]] if soffs[r][p + 1] > soffs[r][p] else 0 for p in range(P)]
+              for r in range(N)]
+    gc.gc_fsdp2_reduce_scatter(gviews, sviews, rows, cols, N, "bf16", "fp32", "avg", "ring")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(N)
+    for p in range(P):
+        for j in sorted({0, 1, N // 2, N - 1}):
+            lo, hi = sh[j][p]
+            n = hi - lo
+            if n == 0:
+                continue
+            k = np.unique(np.concatenate([rng.integers(0, n, size=512), [0, n - 1]]))
+            vals = np.stack([G.normal_bf16(gkeys[i], offs[p] + lo + k, 1e-3) for i in range(N)])
+            want = SM.reduce_positions(vals, "bf16", np.full(len(k), (j + 1) % N), "avg", "fp32")
+            assert_same(_gather(sviews[j][p], k), want, "fp32", f"param {p} owner {j}")
+    del grads, gsh, gviews, sviews
+    psh = arena.alloc(most, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(psh[r], pkeys[r], 0.02)
+    params = arena.alloc(S, "bf16")
+    pviews = [[params[r][offs[p]:offs[p + 1]] for p in range(P)] for r in range(N)]
+    shviews = [[psh[r][soffs[r][p]:soffs[r][p + 1]] if soffs[r][p + 1] > soffs[r][p] else 0 for p in range(P)]
+               for r in range(N)]
+    gc.gc_fsdp2_all_gather(shviews, pviews, rows, cols, N, "bf16")
+    torch.cuda.synchronize()
+    for d in range(1, N):
+        assert torch.equal(params[d].view(torch.int16), params[0].view(torch.int16)), f"rank {d} differs"
+    for p in range(P):
+        n = rows[p] * cols[p]
+        e = np.unique(np.concatenate([rng.integers(0, n, size=4096), [0, n - 1]]))
+        c_rows = -(-rows[p] // N)
+        owner = (e // cols[p]) // c_rows
+        local = e - np.array([sh[o][p][0] for o in owner])
+        want = np.array([G.normal_bf16(pkeys[o], np.array([soffs[o][p] + l]), 0.02)[0] for o, l in zip(owner, local)],
+                        dtype=np.uint16)
+        assert_same(_gather(pviews[N // 3][p], e), want, "bf16", f"all-gather param {p}")
