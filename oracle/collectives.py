@@ -129,12 +129,22 @@ def _ieee(fn):
     return wrapped
 
 
+def _on_wire(part, wire):
+    """What a message carries: the partial rounded to the wire type (bf16), or unchanged."""
+    if wire == "bf16":
+        return bf16_to_f32(f32_to_bf16(part))
+    return part
+
+
 @_ieee
-def ring_reduce_scatter_partials(xs, dtype, chunks=None, trace=None):
+def ring_reduce_scatter_partials(xs, dtype, chunks=None, trace=None, wire=None):
     """Run the ring Reduce-Scatter and return y_j (in the reduction type) for every owner j.
 
     xs[i] is rank i's full buffer.  chunks[j] = (lo, hi) is chunk j's element
-    range; by default owner_chunks(S, N).
+    range; by default owner_chunks(S, N).  wire="bf16": every message is the
+    sender's partial rounded to bf16 (a ring that communicates in the
+    gradient's type; DTLM §11 "精度和分布式通信的关系"), and the receiver adds
+    its own contribution to that rounded value in fp32.
     """
     N = len(xs)
     S = len(xs[0])
@@ -162,7 +172,7 @@ def ring_reduce_scatter_partials(xs, dtype, chunks=None, trace=None):
             if trace is not None:
                 trace.messages.append(Message(s, r, q, k, terms, part.size))
                 trace.sent_elems[r] += part.size
-            delivered[q] = (k, part + piece(q, k), terms + (q,))
+            delivered[q] = (k, _on_wire(part, wire) + piece(q, k), terms + (q,))
         holding = delivered
         if trace is not None:
             trace.steps += 1
@@ -215,8 +225,17 @@ def rank_order_fold(xs, dtype):
     return acc
 
 
+def _ring_wire(order, in_dtype):
+    """(is a ring order, wire type) for order in ring / ring_wire / rank."""
+    if order not in ("ring", "ring_wire", "rank"):
+        raise ValueError("order must be ring, ring_wire or rank")
+    wire = in_dtype if order == "ring_wire" and in_dtype == "bf16" else None
+    return order != "rank", wire
+
+
 def reduce_scatter(xs, in_dtype, out_dtype=None, op="sum", order="ring", trace=None):
-    """Reduce-Scatter with equal chunks: N must divide the per-rank count (the caller pads, as FSDP does)."""
+    """Reduce-Scatter with equal chunks: N must divide the per-rank count (the caller pads, as FSDP does).
+    order "ring_wire" is the ring whose messages are rounded to the input type (bf16 only)."""
     out_dtype = out_dtype or in_dtype
     _check_types(in_dtype, out_dtype, op)
     N = len(xs)
@@ -225,13 +244,12 @@ def reduce_scatter(xs, in_dtype, out_dtype=None, op="sum", order="ring", trace=N
         raise ValueError("reduce_scatter needs a per-rank count divisible by N")
     rc = S // N
     chunks = [(j * rc, (j + 1) * rc) for j in range(N)]
-    if order == "ring":
-        ys = ring_reduce_scatter_partials(xs, in_dtype, chunks, trace)
-    elif order == "rank":
+    ring, wire = _ring_wire(order, in_dtype)
+    if ring:
+        ys = ring_reduce_scatter_partials(xs, in_dtype, chunks, trace, wire)
+    else:
         full = rank_order_fold(xs, in_dtype)
         ys = [full[lo:hi] for lo, hi in chunks]
-    else:
-        raise ValueError("order must be ring or rank")
     return [_epilogue(y, op, N, out_dtype) for y in ys]
 
 
@@ -244,19 +262,19 @@ def all_reduce(xs, dtype, op="sum", order="ring", trace=None):
     """All-Reduce as ring Reduce-Scatter, owner epilogue, ring All-Gather.
 
     order="ring": chunks by owner_chunks (any S), fold order of the ring.
+    order="ring_wire": the same ring, every message rounded to bf16 (bf16 data only).
     order="rank": every element folded in rank order 0..N-1 (no chunk dependence).
     """
     _check_types(dtype, dtype, op)
     N = len(xs)
     S = len(xs[0])
     chunks = owner_chunks(S, N)
-    if order == "ring":
-        ys = ring_reduce_scatter_partials(xs, dtype, chunks, trace)
-    elif order == "rank":
+    ring, wire = _ring_wire(order, dtype)
+    if ring:
+        ys = ring_reduce_scatter_partials(xs, dtype, chunks, trace, wire)
+    else:
         full = rank_order_fold(xs, dtype)
         ys = [full[lo:hi] for lo, hi in chunks]
-    else:
-        raise ValueError("order must be ring or rank")
     shards = [_epilogue(y, op, N, dtype) for y in ys]
     return ring_all_gather(shards, trace)
 

@@ -19,7 +19,7 @@ shards, any lengths.
 import numpy as np
 
 from .buckets import uneven_dim0_shards
-from .collectives import (_check_types, _epilogue, rank_order_fold, ring_all_gather,
+from .collectives import (_check_types, _epilogue, _ring_wire, rank_order_fold, ring_all_gather,
                           ring_reduce_scatter_partials, storage_dtype)
 
 
@@ -39,13 +39,12 @@ def reduce_scatter(grads, rows, cols, in_dtype, out_dtype=None, op="sum", order=
     for p in range(P):
         xs = [np.asarray(grads[r][p]).reshape(-1) for r in range(N)]
         chunks = shard_elems(rows[p], cols[p], N)
-        if order == "ring":
-            ys = ring_reduce_scatter_partials(xs, in_dtype, chunks)
-        elif order == "rank":
+        ring, wire = _ring_wire(order, in_dtype)
+        if ring:
+            ys = ring_reduce_scatter_partials(xs, in_dtype, chunks, wire=wire)
+        else:
             full = rank_order_fold(xs, in_dtype)
             ys = [full[lo:hi] for lo, hi in chunks]
-        else:
-            raise ValueError("order must be ring or rank")
         for j in range(N):
             out[j][p] = _epilogue(ys[j], op, N, out_dtype)
     return out

@@ -12,6 +12,7 @@ step-by-step emulation on sizes where both run.
 import numpy as np
 
 from .collectives import _epilogue, _widen, a2a_recv_offsets, a2a_send_offsets
+from .numerics import bf16_to_f32, f32_to_bf16
 
 
 def fold_start(positions, S, N, order, chunk=None):
@@ -24,11 +25,13 @@ def fold_start(positions, S, N, order, chunk=None):
     return (owner + 1) % N
 
 
-def reduce_positions(values, dtype, starts, op, out_dtype):
+def reduce_positions(values, dtype, starts, op, out_dtype, wire=None):
     """values[i][k] = rank i's input at the k-th sampled position; fold in the given rank order.
 
     Element k is folded as values[start_k], values[start_k + 1], ... (mod N),
     starting from the first term, then averaged and cast like the owner does.
+    wire="bf16": each partial is rounded to bf16 before the next term is added
+    (the ring's messages in the wire type).
     """
     values = np.asarray(values)
     N, m = values.shape
@@ -38,6 +41,8 @@ def reduce_positions(values, dtype, starts, op, out_dtype):
     acc = wide[starts % N, cols].copy()
     with np.errstate(over="ignore", invalid="ignore"):
         for t in range(1, N):
+            if wire == "bf16":
+                acc = bf16_to_f32(f32_to_bf16(acc))
             acc = acc + wide[(starts + t) % N, cols]
     return _epilogue(acc, op, N, out_dtype)
 
@@ -45,15 +50,17 @@ def reduce_positions(values, dtype, starts, op, out_dtype):
 def all_reduce_at(values, positions, S, dtype, op, order):
     """All-reduce outputs at the sampled positions (same value on every rank)."""
     N = np.asarray(values).shape[0]
-    return reduce_positions(values, dtype, fold_start(positions, S, N, order), op, dtype)
+    wire = "bf16" if order == "ring_wire" and dtype == "bf16" else None
+    return reduce_positions(values, dtype, fold_start(positions, S, N, order), op, dtype, wire)
 
 
 def reduce_scatter_at(values, owner, out_pos, recv_count, in_dtype, out_dtype, op, order):
     """Reduce-scatter output recv[owner][out_pos]; values[i][k] = send[i][owner*recv_count + out_pos]."""
     N = np.asarray(values).shape[0]
     owner = np.asarray(owner, dtype=np.int64)
-    starts = (owner + 1) % N if order == "ring" else np.zeros_like(owner)
-    return reduce_positions(values, in_dtype, starts, op, out_dtype)
+    starts = (owner + 1) % N if order != "rank" else np.zeros_like(owner)
+    wire = "bf16" if order == "ring_wire" and in_dtype == "bf16" else None
+    return reduce_positions(values, in_dtype, starts, op, out_dtype, wire)
 
 
 def a2a_source_rows(splits, d, recv_rows):
