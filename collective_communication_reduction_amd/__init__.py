@@ -46,13 +46,13 @@ GC_MAX_RANKS = 64
 GC_OK, GC_ERR_INVALID_ARG, GC_ERR_UNSUPPORTED, GC_ERR_HIP, GC_ERR_NO_MEMORY = range(5)
 GC_INT32, GC_FP32, GC_BF16 = 0, 1, 2
 GC_SUM, GC_AVG = 0, 1
-GC_ORDER_RING, GC_ORDER_RANK = 0, 1
+GC_ORDER_RING, GC_ORDER_RANK, GC_ORDER_RING_WIRE = 0, 1, 2
 GC_AR_FUSED, GC_AR_RS_AG = 0, 1
 SIZE_MAX = (1 << 64) - 1
 
 _DTYPE = {"int32": GC_INT32, "fp32": GC_FP32, "bf16": GC_BF16}
 _OP = {"sum": GC_SUM, "avg": GC_AVG}
-_ORDER = {"ring": GC_ORDER_RING, "rank": GC_ORDER_RANK}
+_ORDER = {"ring": GC_ORDER_RING, "rank": GC_ORDER_RANK, "ring_wire": GC_ORDER_RING_WIRE}
 _ALGO = {"fused": GC_AR_FUSED, "rs_ag": GC_AR_RS_AG}
 
 _vp, _sz, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int

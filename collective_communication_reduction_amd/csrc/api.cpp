@@ -15,7 +15,7 @@ using gci::elem_bytes;
 
 bool valid_dtype(gc_dtype t) { return t == GC_INT32 || t == GC_FP32 || t == GC_BF16; }
 bool valid_op(gc_op op) { return op == GC_SUM || op == GC_AVG; }
-bool valid_order(gc_order o) { return o == GC_ORDER_RING || o == GC_ORDER_RANK; }
+bool valid_order(gc_order o) { return o == GC_ORDER_RING || o == GC_ORDER_RANK || o == GC_ORDER_RING_WIRE; }
 
 uint64_t addr(const void* p) { return reinterpret_cast<uint64_t>(p); }
 
@@ -125,7 +125,8 @@ extern "C" gc_status gc_reduce_scatter(const void* const* send, void* const* rec
     }
   }
   gci::ReduceCall c{send, recv, nranks, N * recv_count, recv_count, in_t, out_t,
-                    op == GC_AVG, order == GC_ORDER_RING, stream};
+                    op == GC_AVG, order != GC_ORDER_RANK, stream};
+  c.wire = order == GC_ORDER_RING_WIRE;
   return gci::launch_reduce_scatter(c);
 }
 
@@ -197,7 +198,8 @@ extern "C" gc_status gc_all_reduce(const void* const* send, void* const* recv, s
 
   const uint64_t c = chunk_len(count, nranks);
   if (algo == GC_AR_FUSED) {
-    gci::ReduceCall call{send, recv, nranks, count, c, t, t, op == GC_AVG, order == GC_ORDER_RING, stream};
+    gci::ReduceCall call{send, recv, nranks, count, c, t, t, op == GC_AVG, order != GC_ORDER_RANK, stream};
+    call.wire = order == GC_ORDER_RING_WIRE;
     return gci::launch_all_reduce(call);
   }
 
@@ -216,7 +218,8 @@ extern "C" gc_status gc_all_reduce(const void* const* send, void* const* recv, s
     shard_out[j] = static_cast<char*>(scratch) + lo * es;
     shard_in[j] = shard_out[j];
   }
-  gci::ReduceCall rs{send, shard_out.data(), nranks, count, c, t, t, op == GC_AVG, order == GC_ORDER_RING, stream};
+  gci::ReduceCall rs{send, shard_out.data(), nranks, count, c, t, t, op == GC_AVG, order != GC_ORDER_RANK, stream};
+  rs.wire = order == GC_ORDER_RING_WIRE;
   GC_TRY(gci::launch_reduce_scatter(rs));
   gci::ReduceCall ag{shard_in.data(), recv, nranks, count, c, t, t, false, false, stream};
   return gci::launch_all_gather(ag);
@@ -380,7 +383,8 @@ extern "C" gc_status gc_fsdp2_reduce_scatter(const void* const* grads, void* con
       out[r] = shards[r * P + p];
     }
     const uint64_t c = (rows[p] + N - 1) / N * cols[p];
-    gci::ReduceCall call{in.data(), out.data(), N, S, c, in_t, out_t, op == GC_AVG, order == GC_ORDER_RING, stream};
+    gci::ReduceCall call{in.data(), out.data(), N, S, c, in_t, out_t, op == GC_AVG, order != GC_ORDER_RANK, stream};
+    call.wire = order == GC_ORDER_RING_WIRE;
     GC_TRY(gci::launch_reduce_scatter(call));
   }
   return GC_OK;
@@ -673,6 +677,7 @@ extern "C" gc_status gc_bucket_all_reduce(const gc_bucket_plan* p, int bucket, v
       !valid_order(order))
     return GC_ERR_INVALID_ARG;
   if (p->t == GC_INT32 && (op == GC_AVG || sumsq)) return GC_ERR_UNSUPPORTED;
+  if (p->t == GC_BF16 && order == GC_ORDER_RING_WIRE) return GC_ERR_UNSUPPORTED;
   if (sumsq && addr(sumsq) % 8) return GC_ERR_INVALID_ARG;
   const size_t T = p->numel.size();
   const size_t es = p->es;
@@ -698,7 +703,7 @@ extern "C" gc_status gc_bucket_all_reduce(const gc_bucket_plan* p, int bucket, v
     for (uint64_t lo = o; lo < o + n;) {
       const uint64_t j = lo / c;
       const uint64_t hi = std::min(o + n, (j + 1) * c);
-      const uint32_t first = order == GC_ORDER_RING ? static_cast<uint32_t>((j + 1) % nranks) : 0u;
+      const uint32_t first = order != GC_ORDER_RANK ? static_cast<uint32_t>((j + 1) % nranks) : 0u;
       pieces.push_back(gci::BucketPiece{lo - o, hi - lo, slot, first});
       lo = hi;
     }

@@ -66,14 +66,24 @@ __device__ __forceinline__ void put(char* p, const Words<Out, VE>& r) {
 
 __device__ __forceinline__ uint32_t next_rank(uint32_t r, uint32_t N) { return r + 1 == N ? 0 : r + 1; }
 
+// A partial as the ring forwards it when WIRE is set: rounded to the input's
+// storage type (bf16, round to nearest even) before the next rank adds its
+// term (DTLM §11: low-precision communication, fp32 arithmetic).  Identity for
+// fp32 and int32 data and when WIRE is clear.
+template <class In, bool WIRE>
+__device__ __forceinline__ typename In::Acc on_wire(typename In::Acc x) {
+  if constexpr (WIRE && In::ES == 2) return __uint_as_float(bf16_bits(x) << 16);
+  else return x;
+}
+
 // `in` points at the N rank pointers (kernel arguments; wavefront-uniform).
-template <class In>
+template <class In, bool WIRE = false>
 __device__ __forceinline__ typename In::Acc fold_one(const char* const* in, uint32_t first, uint32_t N, uint64_t E) {
   typename In::Acc acc = In::one(in[first], E);
   uint32_t r = first;
   for (uint32_t k = 1; k < N; ++k) {
     r = next_rank(r, N);
-    acc = acc + In::one(in[r], E);
+    acc = on_wire<In, WIRE>(acc) + In::one(in[r], E);
   }
   return acc;
 }
@@ -90,7 +100,7 @@ __device__ __forceinline__ void put_one(char* base, uint64_t e, Acc x) {
 // Loads KB ranks' vectors (ranks r, r+1, ... mod N) for the U byte offsets,
 // all issued before the first add, then folds them into acc in that order.
 // FIRST: the batch starts the fold (acc takes the first rank's values).
-template <class In, int KB, int U, bool FIRST>
+template <class In, int KB, int U, bool FIRST, bool WIRE = false>
 __device__ __forceinline__ void fold_batch(const char* const* in, uint32_t& r, uint32_t N, const uint64_t (&off)[U],
                                            typename In::Acc (&acc)[U][In::VE]) {
   constexpr int VE = In::VE;
@@ -114,43 +124,44 @@ __device__ __forceinline__ void fold_batch(const char* const* in, uint32_t& r, u
         for (int l = 0; l < VE; ++l) acc[u][l] = x[l];
       } else {
 #pragma unroll
-        for (int l = 0; l < VE; ++l) acc[u][l] = acc[u][l] + x[l];
+        for (int l = 0; l < VE; ++l) acc[u][l] = on_wire<In, WIRE>(acc[u][l]) + x[l];
       }
     }
   }
 }
 
 // The remaining n (1..7) ranks of a runtime-N fold, as one batch.
-template <class In, int U, bool FIRST>
+template <class In, int U, bool FIRST, bool WIRE = false>
 __device__ __forceinline__ void fold_rest(const char* const* in, uint32_t& r, uint32_t N, uint32_t n,
                                           const uint64_t (&off)[U], typename In::Acc (&acc)[U][In::VE]) {
   switch (n) {
-    case 1: fold_batch<In, 1, U, FIRST>(in, r, N, off, acc); break;
-    case 2: fold_batch<In, 2, U, FIRST>(in, r, N, off, acc); break;
-    case 3: fold_batch<In, 3, U, FIRST>(in, r, N, off, acc); break;
-    case 4: fold_batch<In, 4, U, FIRST>(in, r, N, off, acc); break;
-    case 5: fold_batch<In, 5, U, FIRST>(in, r, N, off, acc); break;
-    case 6: fold_batch<In, 6, U, FIRST>(in, r, N, off, acc); break;
-    case 7: fold_batch<In, 7, U, FIRST>(in, r, N, off, acc); break;
+    case 1: fold_batch<In, 1, U, FIRST, WIRE>(in, r, N, off, acc); break;
+    case 2: fold_batch<In, 2, U, FIRST, WIRE>(in, r, N, off, acc); break;
+    case 3: fold_batch<In, 3, U, FIRST, WIRE>(in, r, N, off, acc); break;
+    case 4: fold_batch<In, 4, U, FIRST, WIRE>(in, r, N, off, acc); break;
+    case 5: fold_batch<In, 5, U, FIRST, WIRE>(in, r, N, off, acc); break;
+    case 6: fold_batch<In, 6, U, FIRST, WIRE>(in, r, N, off, acc); break;
+    case 7: fold_batch<In, 7, U, FIRST, WIRE>(in, r, N, off, acc); break;
     default: break;
   }
 }
 
 // Full fold of U vectors at byte offsets `off` over the N ranks in order
-// first, first+1, ... (mod N).  NF > 0: N fixed at compile time.
-template <class In, int NF, int U>
+// first, first+1, ... (mod N).  NF > 0: N fixed at compile time.  WIRE: every
+// partial is rounded as the ring forwards it before the next term is added.
+template <class In, int NF, int U, bool WIRE = false>
 __device__ __forceinline__ void fold_vec(const char* const* in, uint32_t first, uint32_t N, const uint64_t (&off)[U],
                                          typename In::Acc (&acc)[U][In::VE]) {
   uint32_t r = first;
   if constexpr (NF > 0) {
-    fold_batch<In, NF, U, true>(in, r, NF, off, acc);
+    fold_batch<In, NF, U, true, WIRE>(in, r, NF, off, acc);
   } else if (N >= 8) {
-    fold_batch<In, 8, U, true>(in, r, N, off, acc);
+    fold_batch<In, 8, U, true, WIRE>(in, r, N, off, acc);
     uint32_t k0 = 8;
-    for (; k0 + 8 <= N; k0 += 8) fold_batch<In, 8, U, false>(in, r, N, off, acc);
-    fold_rest<In, U, false>(in, r, N, N - k0, off, acc);
+    for (; k0 + 8 <= N; k0 += 8) fold_batch<In, 8, U, false, WIRE>(in, r, N, off, acc);
+    fold_rest<In, U, false, WIRE>(in, r, N, N - k0, off, acc);
   } else {
-    fold_rest<In, U, true>(in, r, N, N, off, acc);
+    fold_rest<In, U, true, WIRE>(in, r, N, N, off, acc);
   }
 }
 

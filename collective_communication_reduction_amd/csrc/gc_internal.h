@@ -34,6 +34,7 @@ struct ReduceCall {
   bool avg;
   bool ring;
   hipStream_t stream;
+  bool wire = false;  // ring whose forwarded partials are rounded to the input type
 };
 
 gc_status launch_all_reduce(const ReduceCall& call);

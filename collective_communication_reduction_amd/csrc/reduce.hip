@@ -87,7 +87,7 @@ __device__ __forceinline__ uint64_t tile_vec(uint64_t tv0, int u) {
 // compiler keeps every load of a batch in flight together); the chunk's last,
 // partial tile sets GUARD: lanes past the last vector reload that vector and
 // skip their stores.
-template <int KIND, class In, class Out, int NF, int U, bool GUARD, int P>
+template <int KIND, class In, class Out, int NF, int U, bool GUARD, bool WIRE, int P>
 __device__ __forceinline__ void reduce_tile(const RedArgs<P>& a, uint32_t N, uint32_t j, uint32_t first,
                                             const ChunkGeom& g, uint64_t tv0) {
   constexpr int VE = In::VE;
@@ -99,7 +99,7 @@ __device__ __forceinline__ void reduce_tile(const RedArgs<P>& a, uint32_t N, uin
     off[u] = (a.phase + v * VE) * In::ES;
   }
   Acc acc[U][VE];
-  fold_vec<In, NF, U>(a.in, first, N, off, acc);
+  fold_vec<In, NF, U, WIRE>(a.in, first, N, off, acc);
   const bool avg = a.avg != 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -122,8 +122,9 @@ __device__ __forceinline__ void reduce_tile(const RedArgs<P>& a, uint32_t N, uin
 // Fused all-reduce (KIND == kAllReduce: fold N inputs, write N outputs) and
 // reduce-scatter (KIND == kReduceScatter: fold N inputs, write the owner's).
 // NF > 0 fixes N at compile time (N <= 8); NF == 0 reads it from the
-// arguments and folds in batches of eight ranks.
-template <int KIND, class In, class Out, int NF, int U, int P>
+// arguments and folds in batches of eight ranks.  WIRE rounds each forwarded
+// partial to the input type (bf16 ring communicating in bf16).
+template <int KIND, class In, class Out, int NF, int U, bool WIRE, int P>
 __global__ void __launch_bounds__(kThreads) reduce_vec_kernel(const RedArgs<P> a) {
   constexpr int VE = In::VE;
   constexpr int TV = kThreads * U;
@@ -138,9 +139,9 @@ __global__ void __launch_bounds__(kThreads) reduce_vec_kernel(const RedArgs<P> a
     const uint32_t first = a.ring ? next_rank(j, N) : 0;
     const uint64_t tv0 = g.vlo + static_cast<uint64_t>(t) * TV;
     if (tv0 + TV <= g.vhi) {
-      reduce_tile<KIND, In, Out, NF, U, false>(a, N, j, first, g, tv0);
+      reduce_tile<KIND, In, Out, NF, U, false, WIRE>(a, N, j, first, g, tv0);
     } else if (tv0 < g.vhi) {
-      reduce_tile<KIND, In, Out, NF, U, true>(a, N, j, first, g, tv0);
+      reduce_tile<KIND, In, Out, NF, U, true, WIRE>(a, N, j, first, g, tv0);
     }
 
     if (t == 0) {
@@ -152,7 +153,7 @@ __global__ void __launch_bounds__(kThreads) reduce_vec_kernel(const RedArgs<P> a
       const uint64_t nscalar = nhead + (g.hi - tail_beg);
       if (threadIdx.x < nscalar) {
         const uint64_t E = threadIdx.x < nhead ? g.lo + threadIdx.x : tail_beg + (threadIdx.x - nhead);
-        const Acc x = finish(fold_one<In>(a.in, first, N, E), avg, a.nf);
+        const Acc x = finish(fold_one<In, WIRE>(a.in, first, N, E), avg, a.nf);
         if constexpr (KIND == kAllReduce) {
           for (uint32_t q = 0; q < N; ++q) put_one<Out>(a.out[q], E, x);
         } else {
@@ -164,7 +165,7 @@ __global__ void __launch_bounds__(kThreads) reduce_vec_kernel(const RedArgs<P> a
 }
 
 // Element-wise variant for buffers whose relative alignment rules out vectors.
-template <int KIND, class In, class Out, int P>
+template <int KIND, class In, class Out, bool WIRE, int P>
 __global__ void __launch_bounds__(kThreads) reduce_elem_kernel(const RedArgs<P> a) {
   constexpr int TE = kThreads * 4;
   const uint32_t N = a.N;
@@ -179,7 +180,7 @@ __global__ void __launch_bounds__(kThreads) reduce_elem_kernel(const RedArgs<P> 
     for (int u = 0; u < 4; ++u) {
       const uint64_t E = lo + static_cast<uint64_t>(t) * TE + u * kThreads + threadIdx.x;
       if (E < hi) {
-        const typename In::Acc x = finish(fold_one<In>(a.in, first, N, E), avg, a.nf);
+        const typename In::Acc x = finish(fold_one<In, WIRE>(a.in, first, N, E), avg, a.nf);
         if constexpr (KIND == kAllReduce) {
           for (uint32_t r = 0; r < N; ++r) put_one<Out>(a.out[r], E, x);
         } else {
@@ -343,7 +344,7 @@ uint32_t tiles_per_chunk(const gci::ReduceCall& c, int VE, int TV, bool vec, uin
   return static_cast<uint32_t>(std::max<uint64_t>(1, (most + TV - 1) / TV));
 }
 
-template <int KIND, class In, class Out, int U>
+template <int KIND, class In, class Out, int U, bool WIRE>
 gc_status dispatch_reduce(const gci::ReduceCall& c, const Plan& pl) {
   const int N = c.nranks;
   const uint32_t ntiles = static_cast<uint32_t>(N) * pl.tpc;
@@ -352,20 +353,30 @@ gc_status dispatch_reduce(const gci::ReduceCall& c, const Plan& pl) {
     a.phase = pl.phase;
     a.tpc = pl.tpc;
     a.ntiles = ntiles;
-    if (!pl.vec) return launch(reduce_elem_kernel<KIND, In, Out, 8>, a, ntiles, c.stream);
+    if (!pl.vec) return launch(reduce_elem_kernel<KIND, In, Out, WIRE, 8>, a, ntiles, c.stream);
     switch (N) {
-      case 2: return launch(reduce_vec_kernel<KIND, In, Out, 2, U, 8>, a, ntiles, c.stream);
-      case 4: return launch(reduce_vec_kernel<KIND, In, Out, 4, U, 8>, a, ntiles, c.stream);
-      case 8: return launch(reduce_vec_kernel<KIND, In, Out, 8, U, 8>, a, ntiles, c.stream);
-      default: return launch(reduce_vec_kernel<KIND, In, Out, 0, U, 8>, a, ntiles, c.stream);
+      case 2: return launch(reduce_vec_kernel<KIND, In, Out, 2, U, WIRE, 8>, a, ntiles, c.stream);
+      case 4: return launch(reduce_vec_kernel<KIND, In, Out, 4, U, WIRE, 8>, a, ntiles, c.stream);
+      case 8: return launch(reduce_vec_kernel<KIND, In, Out, 8, U, WIRE, 8>, a, ntiles, c.stream);
+      default: return launch(reduce_vec_kernel<KIND, In, Out, 0, U, WIRE, 8>, a, ntiles, c.stream);
     }
   }
   RedArgs<GC_MAX_RANKS> a = make_args<GC_MAX_RANKS>(c);
   a.phase = pl.phase;
   a.tpc = pl.tpc;
   a.ntiles = ntiles;
-  if (!pl.vec) return launch(reduce_elem_kernel<KIND, In, Out, GC_MAX_RANKS>, a, ntiles, c.stream);
-  return launch(reduce_vec_kernel<KIND, In, Out, 0, U, GC_MAX_RANKS>, a, ntiles, c.stream);
+  if (!pl.vec) return launch(reduce_elem_kernel<KIND, In, Out, WIRE, GC_MAX_RANKS>, a, ntiles, c.stream);
+  return launch(reduce_vec_kernel<KIND, In, Out, 0, U, WIRE, GC_MAX_RANKS>, a, ntiles, c.stream);
+}
+
+// The wire-rounding kernels exist for bf16 inputs only; for the other types
+// the rounding is an identity and the plain ring kernels run.
+template <int KIND, class In, class Out, int U>
+gc_status dispatch_wire(const gci::ReduceCall& c, const Plan& pl) {
+  if constexpr (In::ES == 2) {
+    if (c.wire) return dispatch_reduce<KIND, In, Out, U, true>(c, pl);
+  }
+  return dispatch_reduce<KIND, In, Out, U, false>(c, pl);
 }
 
 constexpr int kU = GC_RED_U;
@@ -402,9 +413,9 @@ gc_status run_reduce(const gci::ReduceCall& c) {
   // one vector per thread doubles the workgroup count.
   if (vec && kU > 1 && static_cast<uint64_t>(pl.tpc) * N < kSmallTiles) {
     pl.tpc = tiles_per_chunk(c, VE, kThreads, vec, phase);
-    return dispatch_reduce<KIND, In, Out, 1>(c, pl);
+    return dispatch_wire<KIND, In, Out, 1>(c, pl);
   }
-  return dispatch_reduce<KIND, In, Out, kU>(c, pl);
+  return dispatch_wire<KIND, In, Out, kU>(c, pl);
 }
 
 template <int KIND>

@@ -35,6 +35,15 @@
  * reduce-scatter produces (DTLM §2 "Reduce-Scatter", N = 4 schedule; NXMR
  * §2.2).  GC_ORDER_RANK folds ranks 0, 1, ..., N-1 for every element.  Each
  * fold starts from its first operand, never from zero.
+ *
+ * GC_ORDER_RING_WIRE is the ring order of a ring that communicates in the
+ * gradient's type (DTLM §11 "精度和分布式通信的关系": low-precision
+ * communication, fp32 arithmetic): every partial a rank forwards is rounded to
+ * the input type (bf16: nearest, ties to even) before the next rank adds its
+ * own term in fp32; the owner's last add and the epilogue are as above.  For
+ * fp32 and int32 inputs it equals GC_ORDER_RING.  Accepted by gc_all_reduce,
+ * gc_reduce_scatter and gc_fsdp2_reduce_scatter; gc_bucket_all_reduce
+ * returns GC_ERR_UNSUPPORTED for it on bf16 buckets.
  */
 #ifndef GC_H
 #define GC_H
@@ -59,7 +68,7 @@ typedef enum {
 
 typedef enum { GC_INT32 = 0, GC_FP32 = 1, GC_BF16 = 2 } gc_dtype;
 typedef enum { GC_SUM = 0, GC_AVG = 1 } gc_op;                 /* GC_AVG: floating types only */
-typedef enum { GC_ORDER_RING = 0, GC_ORDER_RANK = 1 } gc_order;
+typedef enum { GC_ORDER_RING = 0, GC_ORDER_RANK = 1, GC_ORDER_RING_WIRE = 2 } gc_order;
 typedef enum { GC_AR_FUSED = 0, GC_AR_RS_AG = 1 } gc_ar_algo;
 
 /*

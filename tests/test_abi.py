@@ -293,3 +293,13 @@ def test_fsdp2_validation():
     bad[2][0] = P_[1][0]
     assert _status(ag, bad, P_, **akw) == gc.GC_ERR_INVALID_ARG
     assert _status(ag, S_, P_, **dict(akw, dtype=9)) == gc.GC_ERR_INVALID_ARG
+
+
+def test_wire_order_rejected_for_bf16_buckets():
+    plan = gc.BucketPlan([8, 8], "bf16", 1 << 20)
+    try:
+        ptrs = _ptrs(4)
+        assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, ptrs, 2, order="ring_wire",
+                       stream=0) == gc.GC_ERR_UNSUPPORTED
+    finally:
+        plan.close()

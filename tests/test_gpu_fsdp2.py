@@ -37,6 +37,8 @@ CASES = [
     (5, [12, 3, 7], [16, 11, 2], "int32", "int32", "sum", "ring"),
     (64, [100, 4096, 7, 64], [32, 1, 5, 8], "bf16", "fp32", "avg", "ring"),          # ranks 2..63 empty for 7 rows
     (3, [0, 4, 0], [5, 3, 0], "fp32", "fp32", "avg", "ring"),                       # empty parameters
+    (8, [17, 5, 1000, 8], [64, 129, 3, 4096], "bf16", "fp32", "avg", "ring_wire"),  # messages rounded to bf16
+    (64, [100, 4096, 7, 64], [32, 1, 5, 8], "bf16", "bf16", "sum", "ring_wire"),
 ]
 
 

@@ -53,7 +53,7 @@ AR_SHAPES = [(1, 5), (2, 1), (3, 2), (4, 0), (4, 4096 * 3 + 13), (5, 12345), (7,
 @pytest.mark.parametrize("dtype,op", [("bf16", "avg"), ("bf16", "sum"), ("fp32", "sum"), ("fp32", "avg"),
                                       ("int32", "sum")])
 @pytest.mark.parametrize("N,S", AR_SHAPES)
-@pytest.mark.parametrize("order", ["ring", "rank"])
+@pytest.mark.parametrize("order", ["ring", "rank", "ring_wire"])
 def test_all_reduce(dtype, op, N, S, order):
     xs = _gen(dtype, N, S, seed=N * 7 + S)
     want = C.all_reduce(xs, dtype, op, order)[0] if S else np.zeros(0)
@@ -100,20 +100,21 @@ def test_all_reduce_in_place(dtype, N):
 
 
 @pytest.mark.parametrize("offsets", [(1, 1, 1, 1), (3, 3, 3, 3), (0, 1, 2, 3), (5, 0, 5, 0)])
-def test_all_reduce_misaligned_views(offsets):
+@pytest.mark.parametrize("order", ["ring", "ring_wire"])
+def test_all_reduce_misaligned_views(offsets, order):
     # views starting k elements into a larger allocation: a common phase keeps
     # the vector path (with unaligned chunk edges); differing phases fall back
     # to the element-wise kernel
     N, S, dtype = 4, 10000 + 17, "bf16"
     xs = _gen(dtype, N, S, seed=5)
-    want = C.all_reduce(xs, dtype, "avg", "ring")[0]
+    want = C.all_reduce(xs, dtype, "avg", order)[0]
     base_in = [empty(S + 8, dtype) for _ in range(N)]
     base_out = [empty(S + 8, dtype) for _ in range(N)]
     send = [b[o:o + S] for b, o in zip(base_in, offsets)]
     recv = [b[o:o + S] for b, o in zip(base_out, offsets)]
     for v, x in zip(send, xs):
         v.copy_(to_dev(x, dtype))
-    gc.gc_all_reduce(send, recv, op="avg")
+    gc.gc_all_reduce(send, recv, op="avg", order=order)
     torch.cuda.synchronize()
     for r in range(N):
         _check(from_dev(recv[r]), want, dtype, f"offsets {offsets}")
@@ -141,7 +142,7 @@ def test_all_reduce_fused_equals_rs_ag_bitwise():
 @pytest.mark.parametrize("tin,tout,op", [("bf16", "fp32", "avg"), ("bf16", "bf16", "avg"), ("fp32", "fp32", "sum"),
                                          ("fp32", "bf16", "avg"), ("int32", "int32", "sum")])
 @pytest.mark.parametrize("N,rc", [(1, 7), (2, 1), (3, 1000), (4, 5), (8, 4096 + 3), (64, 700), (64, 8)])
-@pytest.mark.parametrize("order", ["ring", "rank"])
+@pytest.mark.parametrize("order", ["ring", "rank", "ring_wire"])
 def test_reduce_scatter(tin, tout, op, N, rc, order):
     xs = _gen(tin, N, N * rc, seed=N + rc)
     want = C.reduce_scatter(xs, tin, tout, op, order)

@@ -380,3 +380,90 @@ def test_fsdp2_layer_full(N):
         want = np.array([G.normal_bf16(pkeys[o], np.array([soffs[o][p] + l]), 0.02)[0] for o, l in zip(owner, local)],
                         dtype=np.uint16)
         assert_same(_gather(pviews[N // 3][p], e), want, "bf16", f"all-gather param {p}")
+
+
+def _bf16_nearest(x):
+    """float64 -> bf16 bits with one rounding to nearest even: float64 -> fp32 rounded to
+    odd (truncate, then set the last bit if inexact), then fp32 -> bf16; fp32 keeps more
+    than two bits beyond bf16, so the two steps round like one (Boldo and Melquiond)."""
+    from oracle.numerics import f32_to_bf16
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    over = np.abs(f.astype(np.float64)) > np.abs(x)
+    f = np.where(over, np.nextafter(f, np.float32(0)), f).astype(np.float32)
+    bits = f.view(np.uint32).copy()
+    bits[f.astype(np.float64) != x] |= np.uint32(1)
+    return f32_to_bf16(bits.view(np.float32))
+
+
+def _scaled_error(got, vals_f64, N):
+    """|got - exact mean| / (sum|x| / N): the error relative to the size of the
+    terms, meaningful also where the mean itself cancels to near zero."""
+    exact = vals_f64.sum(axis=0) / N
+    scale = np.maximum(np.abs(vals_f64).sum(axis=0) / N, 1e-300)
+    return np.abs(np.asarray(got, dtype=np.float64) - exact) / scale, exact
+
+
+def test_wire_bf16_ring_error_study():
+    """The ring that forwards bf16 partials against the one that keeps fp32
+    partials, at the full sizes: the 8 x 64 MiB bf16 all-reduce (avg) and the
+    64-rank FSDP layer reduce-scatter (avg, bf16 -> fp32).  Both orders are
+    bit-exact against the oracle on sampled outputs; their errors against the
+    exact mean (float64 sums of the bf16 inputs, exact at these magnitudes) are
+    printed, and the wire ring's must be the larger."""
+    from oracle.numerics import bf16_to_f32
+    cfg = WORKLOADS["ar_bf16_n8"]
+    N, S = cfg["nranks"], cfg["count"]
+    keys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    arena = gc.RankArena(N)
+    send = arena.alloc(S, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(send[r], keys[r], cfg["sigma"])
+    pos = _positions(S, N, np.random.default_rng(21), m=1 << 17)
+    vals = np.stack([G.normal_bf16(keys[i], pos, cfg["sigma"]) for i in range(N)])
+    wide = bf16_to_f32(vals).astype(np.float64)
+    stats = {}
+    for order in ("ring", "ring_wire"):
+        recv = arena.alloc(S, "bf16")
+        gc.gc_all_reduce(send, recv, op="avg", order=order)
+        torch.cuda.synchronize()
+        got = _gather(recv[N // 2], pos)
+        assert_same(got, SM.all_reduce_at(vals, pos, S, "bf16", "avg", order), "bf16", f"all-reduce {order}")
+        err, exact = _scaled_error(bf16_to_f32(got), wide, N)
+        off = float(np.mean(_bf16_nearest(exact) != got))         # vs the exact mean rounded once
+        stats[order] = (off, float(np.median(err)), float(np.quantile(err, 0.99)), float(err.max()))
+        print(f"ar_bf16_n8 {order}: differs from the correctly rounded mean {off:.4%}; error / mean|x|: "
+              f"median {stats[order][1]:.3e}, p99 {stats[order][2]:.3e}, max {stats[order][3]:.3e} "
+              f"({len(pos)} samples)", flush=True)
+    assert stats["ring_wire"][1] > stats["ring"][1] and stats["ring_wire"][0] > stats["ring"][0]
+    del send, recv
+    torch.cuda.empty_cache()
+
+    N = WORKLOADS["fsdp_layer_n64"]["nranks"]
+    numels = [n for _, n in fsdp_layer_tensors()]
+    _, _, S, _ = OB.flat_param_shards(numels, N)
+    rc = S // N
+    gkeys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    arena = gc.RankArena(N)
+    grads = arena.alloc(S, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(grads[r], gkeys[r], 1e-3)
+    rng = np.random.default_rng(22)
+    owners = list(range(0, N, 9))
+    ks = {j: np.unique(rng.integers(0, rc, size=4096)) for j in owners}
+    vals = {j: np.stack([G.normal_bf16(gkeys[i], j * rc + ks[j], 1e-3) for i in range(N)]) for j in owners}
+    for order in ("ring", "ring_wire"):
+        shards = arena.alloc(rc, "fp32")
+        gc.gc_reduce_scatter(grads, shards, op="avg", order=order)
+        torch.cuda.synchronize()
+        rel = []
+        for j in owners:
+            want = SM.reduce_scatter_at(vals[j], np.full(len(ks[j]), j), ks[j], rc, "bf16", "fp32", "avg", order)
+            got = _gather(shards[j], ks[j])
+            assert_same(got, want, "fp32", f"reduce-scatter {order} owner {j}")
+            rel.append(_scaled_error(got, bf16_to_f32(vals[j]).astype(np.float64), N)[0])
+        rel = np.concatenate(rel)
+        stats[order + "64"] = (float(np.median(rel)), float(np.quantile(rel, 0.99)), float(rel.max()))
+        print(f"fsdp_layer_n64 {order}: error / mean|x|: median {stats[order + '64'][0]:.3e}, "
+              f"p99 {stats[order + '64'][1]:.3e}, max {stats[order + '64'][2]:.3e} ({len(rel)} samples)", flush=True)
+    assert stats["ring_wire64"][0] > 10 * stats["ring64"][0] and stats["ring_wire64"][2] > stats["ring64"][2]
