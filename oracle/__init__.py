@@ -28,6 +28,8 @@ Modules
                flatten / pad / shard, zero-copy bucket all-reduce, sum of squares
   fsdp2        FSDP2 per-parameter Shard(0) reduce-scatter / all-gather with
                uneven and empty shards
+  hierarchical two-level all-reduce over rank groups and the HSDP gradient
+               reduce-scatter
   moe          expert-parallel MoE around the all-to-all: routing plan,
                dispatch from token order, weighted combine back to token order
   sampled      evaluation of single output elements, for checks at sizes the
@@ -42,4 +44,4 @@ recorded as such, pinned by hand-worked examples and the invariants they must
 satisfy.
 """
 
-from . import numerics, collectives, buckets, sampled, cost_model, moe, fsdp2  # noqa: F401
+from . import numerics, collectives, buckets, sampled, cost_model, moe, fsdp2, hierarchical  # noqa: F401
