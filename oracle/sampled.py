@@ -86,3 +86,44 @@ def a2a_source_rows(splits, d, recv_rows):
         if not found:
             raise IndexError("row beyond the receive buffer")
     return out_s, out_row
+
+
+def hier_fold_starts(positions, count, S, R, order, chunk=None):
+    """(first group, first member) of the two-level fold of each element position.
+
+    Element E lies in chunk i of the S chunks of length c1 = ceil(count / S)
+    (or `chunk`) and in piece h of that chunk's R pieces of ceil(len_i / R);
+    the ring folds groups from h + 1 and members from i + 1 (rank order: 0, 0).
+    """
+    positions = np.asarray(positions, dtype=np.int64)
+    if order == "rank":
+        z = np.zeros(positions.shape, dtype=np.int64)
+        return z, z
+    c1 = chunk if chunk is not None else (-(-count // S) if count else 1)
+    i = positions // c1
+    lo = np.minimum(count, i * c1)
+    L = np.minimum(count, lo + c1) - lo
+    c2 = np.maximum(1, -(-L // R))
+    h = (positions - lo) // c2
+    return (h + 1) % R, (i + 1) % S
+
+
+def hier_reduce_positions(values, S, g0, m0, dtype, op, out_dtype):
+    """values[r][k]: rank r's input at the k-th sampled position (rank r = g * S + i).
+    Groups folded from g0, each group's members from m0, fp32 partials, one epilogue."""
+    values = np.asarray(values)
+    N, m = values.shape
+    R = N // S
+    wide = np.stack([_widen(values[r], dtype) for r in range(N)])
+    cols = np.arange(m)
+    g0 = np.asarray(g0, dtype=np.int64)
+    m0 = np.asarray(m0, dtype=np.int64)
+    total = None
+    with np.errstate(over="ignore", invalid="ignore"):
+        for q in range(R):
+            g = (g0 + q) % R
+            part = wide[g * S + m0, cols].copy()
+            for t in range(1, S):
+                part = part + wide[g * S + (m0 + t) % S, cols]
+            total = part if total is None else total + part
+    return _epilogue(total, op, N, out_dtype)

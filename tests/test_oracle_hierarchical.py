@@ -82,3 +82,22 @@ def test_group_size_must_divide():
         H.all_reduce([np.zeros(3, np.float32)] * 6, 4, "fp32")
     with pytest.raises(ValueError):
         H.hsdp_reduce_scatter([np.zeros(3, np.float32)] * 4, 2, "fp32")
+
+
+@pytest.mark.parametrize("R,S,count", [(2, 8, 301), (4, 3, 50), (3, 4, 7), (2, 2, 1), (2, 8, 320), (4, 3, 51)])
+@pytest.mark.parametrize("order", ["ring", "rank"])
+def test_sampled_two_level_matches_emulation(R, S, count, order):
+    from oracle import sampled as SM
+    rng = np.random.default_rng(R + S + count)
+    xs = [f32_to_bf16(rng.normal(size=count).astype(np.float32)) for _ in range(R * S)]
+    full = H.all_reduce(xs, S, "bf16", "avg", order)[0]
+    pos = np.arange(count)
+    g0, m0 = SM.hier_fold_starts(pos, count, S, R, order)
+    got = SM.hier_reduce_positions(np.stack([x[pos] for x in xs]), S, g0, m0, "bf16", "avg", "bf16")
+    assert np.array_equal(got, full)
+    if count % S == 0:
+        rc = count // S
+        sh = H.hsdp_reduce_scatter(xs, S, "bf16", "fp32", "avg", order)
+        g0, m0 = SM.hier_fold_starts(pos, count, S, R, order, chunk=rc)
+        got = SM.hier_reduce_positions(np.stack([x[pos] for x in xs]), S, g0, m0, "bf16", "avg", "fp32")
+        assert np.array_equal(got, np.concatenate([sh[i] for i in range(S)]))
