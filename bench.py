@@ -19,7 +19,8 @@ same way; the zero-copy DDP step all-reduces each bucket in place over the
 gradient tensors instead of packing and unpacking it), and moe_ep_n8 (the
 expert-parallel MoE data flow: routing plan, dispatch from token order and
 weighted combine back to token order, identity experts), and fsdp2_layer_n64
-(the FSDP layer sharded per parameter on dim 0, as FSDP2 does).
+(the FSDP layer sharded per parameter on dim 0, as FSDP2 does), and hier_ar_n16
+(the two-level all-reduce of 16 ranks as two groups of eight).
 """
 
 import argparse
@@ -43,10 +44,11 @@ KERNEL_SOURCES = {
     "bucket": [CSRC + "bucket.hip", CSRC + "fold.h", CSRC + "device_common.h"],
     "a2a": [CSRC + "movement.hip", CSRC + "device_common.h"],
     "moe": [CSRC + "moe.hip", CSRC + "fold.h", CSRC + "device_common.h"],
+    "hier": [CSRC + "hier.hip", CSRC + "fold.h", CSRC + "device_common.h"],
 }
 WORKLOAD_KERNELS = {"ar_bf16_n8": "reduce", "ar_fp32_n4": "reduce", "ddp_llama7b": "reduce",
                     "fsdp_layer_n64": "reduce", "ddp_llama7b_zero_copy": "bucket", "moe_a2a_n8": "a2a",
-                    "moe_ep_n8": "moe", "fsdp2_layer_n64": "reduce"}
+                    "moe_ep_n8": "moe", "fsdp2_layer_n64": "reduce", "hier_ar_n16": "hier"}
 
 
 def parse():
@@ -56,7 +58,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ar_bf16_n8",
                    choices=["ar_bf16_n8", "ar_fp32_n4", "ddp_llama7b", "ddp_llama7b_zero_copy", "fsdp_layer_n64",
-                            "moe_a2a_n8", "moe_ep_n8", "fsdp2_layer_n64"])
+                            "moe_a2a_n8", "moe_ep_n8", "fsdp2_layer_n64", "hier_ar_n16"])
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--layout", default="arena", choices=["arena", "staggered", "separate"],
                    help="placement of the rank buffers in HBM")
@@ -438,6 +440,52 @@ class Fsdp2Workload(Workload):
         return run, nbytes, "oracle per-parameter ring reduce-scatter of 64 ranks x (q_proj 4096x4096 + 2 x 4096) bf16"
 
 
+class HierWorkload(Workload):
+    """Two-level all-reduce, 16 ranks as 2 groups of 8 (two nodes of eight GPUs), 64 MiB bf16 each, avg."""
+
+    def __init__(self, args):
+        import torch
+        import collective_communication_reduction_amd as gc
+        from gen import device as GD
+        from gen.workloads import WORKLOADS
+        self.gc = gc
+        cfg = WORKLOADS["hier_ar_n16"]
+        self.cfg = cfg
+        self.N, self.S, self.count = cfg["nranks"], cfg["group"], cfg["count"]
+        self.name = "hier_ar_n16"
+        L = Layout(args, self.N)
+        self.layout = L.name()
+        self.send = L.buffers(self.count, torch.bfloat16)
+        self.recv = L.buffers(self.count, torch.bfloat16)
+        for r in range(self.N):
+            GD.fill_normal_bf16(self.send[r], _keyed(args.seed, r), cfg["sigma"])
+        self.sp, self.rp = gc.gc_pointers(self.send), gc.gc_pointers(self.recv)
+        self.bytes_per_step = 2 * self.N * self.count * 2
+        self.dominant = "hier_vec_kernel (fused two-level all-reduce)"
+        self.dominant_bytes = self.bytes_per_step
+        torch.cuda.synchronize()
+
+    def step(self, k):
+        self.gc.gc_hier_all_reduce(self.sp, self.rp, self.S, op="avg", order="ring", count=self.count,
+                                   dtype="bf16")
+
+    def config(self):
+        return {"workload": self.name, "nranks": self.N, "groups": self.N // self.S, "group_size": self.S,
+                "count_per_rank": self.count, "storage": "bf16", "op": "avg", "order": "ring (two-level)",
+                "layout": self.layout}
+
+    def cpu_sample(self, seed):
+        import numpy as np
+        from gen import host as G
+        from oracle import hierarchical as H
+        m = 1 << 23  # the first quarter (8,388,608 elements) of each rank
+        xs = [G.normal_bf16(_keyed(seed, r), np.arange(m, dtype=np.uint64), self.cfg["sigma"]) for r in range(self.N)]
+
+        def run():
+            return H.all_reduce(xs, self.S, "bf16", "avg", "ring")
+        return run, 2 * self.N * m * 2, f"oracle three-ring two-level all-reduce of 16 ranks x {m} bf16"
+
+
 class MoeWorkload(Workload):
     """MoE dispatch all-to-all, 8 ranks x 16384 tokens x 4096 bf16, top-2 of 64 experts, Zipf(1.1)."""
 
@@ -616,6 +664,8 @@ def make(args):
         return MoeEpWorkload(args)
     if args.workload == "fsdp2_layer_n64":
         return Fsdp2Workload(args)
+    if args.workload == "hier_ar_n16":
+        return HierWorkload(args)
     return MoeWorkload(args)
 
 

@@ -74,6 +74,8 @@ _c_a2a = _sig("gc_all_to_all", _int, _VPP, _VPP, ctypes.POINTER(ctypes.c_int64),
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _SZP = ctypes.POINTER(ctypes.c_size_t)
 _c_fsdp2_rs = _sig("gc_fsdp2_reduce_scatter", _int, _VPP, _VPP, _SZP, _SZP, _int, _int, _int, _int, _int, _int, _vp)
+_c_hier_ar = _sig("gc_hier_all_reduce", _int, _VPP, _VPP, _sz, _int, _int, _int, _int, _int, _vp)
+_c_hsdp_rs = _sig("gc_hsdp_reduce_scatter", _int, _VPP, _VPP, _sz, _int, _int, _int, _int, _int, _int, _vp)
 _c_fsdp2_ag = _sig("gc_fsdp2_all_gather", _int, _VPP, _VPP, _SZP, _SZP, _int, _int, _int, _vp)
 _c_moe_scratch = _sig("gc_moe_route_scratch_bytes", _sz, _I64P, _int, _int, _int)
 _c_moe_route = _sig("gc_moe_route", _int, _VPP, _I64P, _int, _int, _int, _vp, _VPP, _vp, _sz, _vp)
@@ -247,6 +249,27 @@ def gc_all_to_all(send, recv, splits, row_bytes, stream=None):
     n, _, e = sp.shape
     _check(_c_a2a(_ptr_array(send), _ptr_array(recv), sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, e,
                   int(row_bytes), _stream(stream, _first(send))), "gc_all_to_all")
+    return recv
+
+
+def gc_hier_all_reduce(send, recv, group_size, op="avg", order="ring", count=None, dtype=None, stream=None):
+    """Two-level all-reduce over len(send) = R * group_size ranks (member i of group g = rank g*group_size + i)."""
+    n = len(send)
+    _check(_c_hier_ar(_ptr_array(send), _ptr_array(recv), _numel(send, count), n, int(group_size),
+                      _infer_dtype(send, dtype), _enum(_OP, op), _enum(_ORDER, order), _stream(stream, _first(send))),
+           "gc_hier_all_reduce")
+    return recv
+
+
+def gc_hsdp_reduce_scatter(send, recv, group_size, op="avg", order="ring", recv_count=None, in_dtype=None,
+                           out_dtype=None, stream=None):
+    """HSDP gradient reduce-scatter: recv[r] = chunk (r mod group_size) of the reduction over all ranks."""
+    n = len(send)
+    rc = int(recv_count) if recv_count is not None else int(recv[0].numel())
+    tin = _infer_dtype(send, in_dtype)
+    tout = _infer_dtype(recv, out_dtype)
+    _check(_c_hsdp_rs(_ptr_array(send), _ptr_array(recv), rc, n, int(group_size), tin, tout, _enum(_OP, op),
+                      _enum(_ORDER, order), _stream(stream, _first(send))), "gc_hsdp_reduce_scatter")
     return recv
 
 

@@ -30,7 +30,7 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
-LIB_SOURCES = ["api.cpp", "reduce.hip", "movement.hip", "bucket.hip", "moe.hip"]
+LIB_SOURCES = ["api.cpp", "reduce.hip", "movement.hip", "bucket.hip", "moe.hip", "hier.hip"]
 
 
 def _hipcc():

@@ -283,6 +283,74 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
   return GC_OK;
 }
 
+// ------------------------------------------------------- two-level / HSDP
+
+namespace {
+
+gc_status check_mesh(int nranks, int group_size, gc_order order, gc_dtype t) {
+  GC_TRY(check_ranks(nranks));
+  if (group_size < 1 || nranks % group_size) return GC_ERR_INVALID_ARG;
+  if (order == GC_ORDER_RING_WIRE && t == GC_BF16) return GC_ERR_UNSUPPORTED;
+  return GC_OK;
+}
+
+}  // namespace
+
+extern "C" gc_status gc_hier_all_reduce(const void* const* send, void* const* recv, size_t count, int nranks,
+                                        int group_size, gc_dtype t, gc_op op, gc_order order, hipStream_t stream) {
+  if (!valid_dtype(t) || !valid_op(op) || !valid_order(order) || !send || !recv) return GC_ERR_INVALID_ARG;
+  GC_TRY(check_mesh(nranks, group_size, order, t));
+  if (op == GC_AVG && t == GC_INT32) return GC_ERR_UNSUPPORTED;
+  if (mul_overflows(count, 4)) return GC_ERR_INVALID_ARG;
+  if (count == 0) return GC_OK;
+  const size_t es = elem_bytes(t);
+  GC_TRY(check_ptrs(send, nranks, es));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es));
+  // Aliasing as gc_all_reduce: each recv[r] is disjoint from every send[i] or equal to it.
+  const uint64_t bytes = count * es;
+  std::vector<Span> outs;
+  for (int r = 0; r < nranks; ++r) outs.push_back(span(recv[r], bytes));
+  if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
+  for (int r = 0; r < nranks; ++r)
+    for (int i = 0; i < nranks; ++i)
+      if (overlaps(outs[r], span(send[i], bytes)) && addr(recv[r]) != addr(send[i])) return GC_ERR_INVALID_ARG;
+  gci::HierCall call{send, recv, nranks, group_size, count, t, t, op == GC_AVG, order != GC_ORDER_RANK, stream};
+  return gci::launch_hier_all_reduce(call);
+}
+
+extern "C" gc_status gc_hsdp_reduce_scatter(const void* const* send, void* const* recv, size_t recv_count,
+                                            int nranks, int group_size, gc_dtype in_t, gc_dtype out_t, gc_op op,
+                                            gc_order order, hipStream_t stream) {
+  if (!valid_dtype(in_t) || !valid_dtype(out_t) || !valid_op(op) || !valid_order(order) || !send || !recv)
+    return GC_ERR_INVALID_ARG;
+  GC_TRY(check_mesh(nranks, group_size, order, in_t));
+  if ((in_t == GC_INT32) != (out_t == GC_INT32)) return GC_ERR_UNSUPPORTED;
+  if (op == GC_AVG && in_t == GC_INT32) return GC_ERR_UNSUPPORTED;
+  const uint64_t S = static_cast<uint64_t>(group_size);
+  if (mul_overflows(recv_count, S) || mul_overflows(recv_count * S, 4)) return GC_ERR_INVALID_ARG;
+  if (recv_count == 0) return GC_OK;
+  const size_t ei = elem_bytes(in_t), eo = elem_bytes(out_t);
+  GC_TRY(check_ptrs(send, nranks, ei));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, eo));
+  // Aliasing: recv[r] may sit exactly on member i's chunk of send[r] (i = r mod
+  // group) when the types match; no other overlap.
+  std::vector<Span> outs;
+  for (int r = 0; r < nranks; ++r) outs.push_back(span(recv[r], recv_count * eo));
+  if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
+  for (int r = 0; r < nranks; ++r) {
+    const uint64_t i = static_cast<uint64_t>(r % group_size);
+    const bool in_place = in_t == out_t && addr(recv[r]) == addr(send[r]) + i * recv_count * ei;
+    for (int q = 0; q < nranks; ++q) {
+      if (!overlaps(outs[r], span(send[q], S * recv_count * ei))) continue;
+      if (in_place && q == r) continue;
+      return GC_ERR_INVALID_ARG;
+    }
+  }
+  gci::HierCall call{send, recv, nranks, group_size, S * recv_count, in_t, out_t, op == GC_AVG,
+                     order != GC_ORDER_RANK, stream};
+  return gci::launch_hsdp_reduce_scatter(call);
+}
+
 // ------------------------------------------------------------- FSDP2 Shard(0)
 
 namespace {

@@ -77,13 +77,15 @@ __device__ __forceinline__ typename In::Acc on_wire(typename In::Acc x) {
 }
 
 // `in` points at the N rank pointers (kernel arguments; wavefront-uniform).
+// base: index of rank 0 of the folded set in `in` (a group of a larger mesh).
 template <class In, bool WIRE = false>
-__device__ __forceinline__ typename In::Acc fold_one(const char* const* in, uint32_t first, uint32_t N, uint64_t E) {
-  typename In::Acc acc = In::one(in[first], E);
+__device__ __forceinline__ typename In::Acc fold_one(const char* const* in, uint32_t first, uint32_t N, uint64_t E,
+                                                     uint32_t base = 0) {
+  typename In::Acc acc = In::one(in[base + first], E);
   uint32_t r = first;
   for (uint32_t k = 1; k < N; ++k) {
     r = next_rank(r, N);
-    acc = on_wire<In, WIRE>(acc) + In::one(in[r], E);
+    acc = on_wire<In, WIRE>(acc) + In::one(in[base + r], E);
   }
   return acc;
 }
@@ -102,13 +104,13 @@ __device__ __forceinline__ void put_one(char* base, uint64_t e, Acc x) {
 // FIRST: the batch starts the fold (acc takes the first rank's values).
 template <class In, int KB, int U, bool FIRST, bool WIRE = false>
 __device__ __forceinline__ void fold_batch(const char* const* in, uint32_t& r, uint32_t N, const uint64_t (&off)[U],
-                                           typename In::Acc (&acc)[U][In::VE]) {
+                                           typename In::Acc (&acc)[U][In::VE], uint32_t rank0 = 0) {
   constexpr int VE = In::VE;
   typedef typename In::Acc Acc;
   u32x4 raw[KB][U];
 #pragma unroll
   for (int k = 0; k < KB; ++k) {
-    const char* base = in[r];
+    const char* base = in[rank0 + r];
 #pragma unroll
     for (int u = 0; u < U; ++u) raw[k][u] = ld16(base + off[u]);
     r = next_rank(r, N);
@@ -133,15 +135,16 @@ __device__ __forceinline__ void fold_batch(const char* const* in, uint32_t& r, u
 // The remaining n (1..7) ranks of a runtime-N fold, as one batch.
 template <class In, int U, bool FIRST, bool WIRE = false>
 __device__ __forceinline__ void fold_rest(const char* const* in, uint32_t& r, uint32_t N, uint32_t n,
-                                          const uint64_t (&off)[U], typename In::Acc (&acc)[U][In::VE]) {
+                                          const uint64_t (&off)[U], typename In::Acc (&acc)[U][In::VE],
+                                          uint32_t rank0 = 0) {
   switch (n) {
-    case 1: fold_batch<In, 1, U, FIRST, WIRE>(in, r, N, off, acc); break;
-    case 2: fold_batch<In, 2, U, FIRST, WIRE>(in, r, N, off, acc); break;
-    case 3: fold_batch<In, 3, U, FIRST, WIRE>(in, r, N, off, acc); break;
-    case 4: fold_batch<In, 4, U, FIRST, WIRE>(in, r, N, off, acc); break;
-    case 5: fold_batch<In, 5, U, FIRST, WIRE>(in, r, N, off, acc); break;
-    case 6: fold_batch<In, 6, U, FIRST, WIRE>(in, r, N, off, acc); break;
-    case 7: fold_batch<In, 7, U, FIRST, WIRE>(in, r, N, off, acc); break;
+    case 1: fold_batch<In, 1, U, FIRST, WIRE>(in, r, N, off, acc, rank0); break;
+    case 2: fold_batch<In, 2, U, FIRST, WIRE>(in, r, N, off, acc, rank0); break;
+    case 3: fold_batch<In, 3, U, FIRST, WIRE>(in, r, N, off, acc, rank0); break;
+    case 4: fold_batch<In, 4, U, FIRST, WIRE>(in, r, N, off, acc, rank0); break;
+    case 5: fold_batch<In, 5, U, FIRST, WIRE>(in, r, N, off, acc, rank0); break;
+    case 6: fold_batch<In, 6, U, FIRST, WIRE>(in, r, N, off, acc, rank0); break;
+    case 7: fold_batch<In, 7, U, FIRST, WIRE>(in, r, N, off, acc, rank0); break;
     default: break;
   }
 }
@@ -149,19 +152,20 @@ __device__ __forceinline__ void fold_rest(const char* const* in, uint32_t& r, ui
 // Full fold of U vectors at byte offsets `off` over the N ranks in order
 // first, first+1, ... (mod N).  NF > 0: N fixed at compile time.  WIRE: every
 // partial is rounded as the ring forwards it before the next term is added.
+// rank0: index in `in` of the folded set's rank 0 (a group of a larger mesh).
 template <class In, int NF, int U, bool WIRE = false>
 __device__ __forceinline__ void fold_vec(const char* const* in, uint32_t first, uint32_t N, const uint64_t (&off)[U],
-                                         typename In::Acc (&acc)[U][In::VE]) {
+                                         typename In::Acc (&acc)[U][In::VE], uint32_t rank0 = 0) {
   uint32_t r = first;
   if constexpr (NF > 0) {
-    fold_batch<In, NF, U, true, WIRE>(in, r, NF, off, acc);
+    fold_batch<In, NF, U, true, WIRE>(in, r, NF, off, acc, rank0);
   } else if (N >= 8) {
-    fold_batch<In, 8, U, true, WIRE>(in, r, N, off, acc);
+    fold_batch<In, 8, U, true, WIRE>(in, r, N, off, acc, rank0);
     uint32_t k0 = 8;
-    for (; k0 + 8 <= N; k0 += 8) fold_batch<In, 8, U, false, WIRE>(in, r, N, off, acc);
-    fold_rest<In, U, false, WIRE>(in, r, N, N - k0, off, acc);
+    for (; k0 + 8 <= N; k0 += 8) fold_batch<In, 8, U, false, WIRE>(in, r, N, off, acc, rank0);
+    fold_rest<In, U, false, WIRE>(in, r, N, N - k0, off, acc, rank0);
   } else {
-    fold_rest<In, U, true, WIRE>(in, r, N, N, off, acc);
+    fold_rest<In, U, true, WIRE>(in, r, N, N, off, acc, rank0);
   }
 }
 

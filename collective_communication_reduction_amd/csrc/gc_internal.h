@@ -38,6 +38,26 @@ struct ReduceCall {
 };
 
 gc_status launch_all_reduce(const ReduceCall& call);
+
+// Two-level reduction over nranks = R * group ranks (rank g * group + i is
+// member i of group g).  in[r]: rank r's count elements.  All-reduce: out[r]
+// rank r's count elements.  HSDP reduce-scatter: out[r] member i's shard of
+// count / group elements.
+struct HierCall {
+  const void* const* in;
+  void* const* out;
+  int nranks;
+  int group;
+  uint64_t count;
+  gc_dtype in_t;
+  gc_dtype out_t;
+  bool avg;
+  bool ring;
+  hipStream_t stream;
+};
+
+gc_status launch_hier_all_reduce(const HierCall& call);
+gc_status launch_hsdp_reduce_scatter(const HierCall& call);
 gc_status launch_reduce_scatter(const ReduceCall& call);
 gc_status launch_all_gather(const ReduceCall& call);
 

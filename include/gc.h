@@ -141,6 +141,39 @@ gc_status gc_all_to_all(const void* const* send, void* const* recv, const int64_
                         int nranks, int experts_per_rank, size_t row_bytes, hipStream_t stream);
 
 /*
+ * Two-level (hierarchical) all-reduce and HSDP (AIG6 Table 6-2: hierarchical
+ * all-reduce, two-level aggregation matched to the topology; AIG6 §6.3.6:
+ * HSDP on nodes of 8 GPUs; DTLM §4: an HSDP mesh has a shard dimension and a
+ * replicate dimension).  nranks = R * group_size ranks form R groups; rank
+ * g * group_size + i is member i of group g (the mesh's shard index).
+ *
+ * The result is bit-identical to the three-ring schedule: inside each group a
+ * ring reduce-scatter over its members (member i keeps chunk i of the group's
+ * sum, chunks c1 = ceil(count / group_size) long, fp32 partials), then for
+ * each i a ring all-reduce of chunk i across the R groups (chunk i cut into R
+ * pieces of ceil(len_i / R); piece h folded from group h+1 around to group h),
+ * then an all-gather inside each group.  The epilogue runs once at the end
+ * (GC_AVG divides by nranks).  GC_ORDER_RANK folds members 0.. and groups 0..
+ * instead.  GC_ORDER_RING_WIRE is GC_ERR_UNSUPPORTED for bf16 (for fp32 and
+ * int32 it is the ring).  One pass: every input is read once and every output
+ * written once.  Types and aliasing as gc_all_reduce.
+ */
+gc_status gc_hier_all_reduce(const void* const* send, void* const* recv, size_t count, int nranks, int group_size,
+                             gc_dtype t, gc_op op, gc_order order, hipStream_t stream);
+
+/*
+ * HSDP gradient reduce-scatter: the first two phases of gc_hier_all_reduce.
+ *   send[r]  rank r's full gradient, group_size * recv_count elements of in_t.
+ *   recv[r]  recv_count elements of out_t: chunk i = r mod group_size of the
+ *            reduction over all nranks ranks, the same on every group.
+ * Types, op and padding as gc_reduce_scatter (group_size divides the length).
+ * recv[r] may sit exactly on chunk i of send[r] when in_t == out_t.
+ */
+gc_status gc_hsdp_reduce_scatter(const void* const* send, void* const* recv, size_t recv_count, int nranks,
+                                 int group_size, gc_dtype in_t, gc_dtype out_t, gc_op op, gc_order order,
+                                 hipStream_t stream);
+
+/*
  * FSDP2 per-parameter Shard(0) (DTLM §4 "FSDP2: DTensor / DeviceMesh"): each of
  * nparams parameters, rows[p] x cols[p] elements stored row-major, is its own
  * sharded tensor.  Rank r's shard of parameter p is rows [min(R, r*c),

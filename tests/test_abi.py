@@ -303,3 +303,25 @@ def test_wire_order_rejected_for_bf16_buckets():
                        stream=0) == gc.GC_ERR_UNSUPPORTED
     finally:
         plan.close()
+
+
+def test_hier_and_hsdp_validation():
+    har, hrs = gc.gc_hier_all_reduce, gc.gc_hsdp_reduce_scatter
+    s, r = _ptrs(8), _ptrs(8, base=FAKE + (1 << 40))
+    assert _status(har, s, r, 4, count=0, dtype="bf16", stream=0) == gc.GC_OK
+    assert _status(har, s, r, 3, count=16, dtype="bf16", stream=0) == gc.GC_ERR_INVALID_ARG     # 3 does not divide 8
+    assert _status(har, s, r, 0, count=16, dtype="bf16", stream=0) == gc.GC_ERR_INVALID_ARG
+    assert _status(har, s, r, 4, count=16, dtype="bf16", order="ring_wire", stream=0) == gc.GC_ERR_UNSUPPORTED
+    assert _status(har, s, r, 4, count=16, dtype="int32", op="avg", stream=0) == gc.GC_ERR_UNSUPPORTED
+    assert _status(har, s, r[:7] + [r[6] + 8], 4, count=16, dtype="fp32", stream=0) == gc.GC_ERR_INVALID_ARG
+    assert _status(har, s, r[:7] + [s[3] + 4], 4, count=16, dtype="fp32", stream=0) == gc.GC_ERR_INVALID_ARG
+    kw = dict(recv_count=10, in_dtype="bf16", out_dtype="fp32", stream=0)
+    assert _status(hrs, s, r, 4, **dict(kw, in_dtype="int32")) == gc.GC_ERR_UNSUPPORTED
+    assert _status(hrs, s, r, 5, **kw) == gc.GC_ERR_INVALID_ARG
+    assert _status(hrs, s, r[:7] + [r[7] + 2], 4, **kw) == gc.GC_ERR_INVALID_ARG                 # misaligned fp32
+    # in place only at member i's chunk of the same rank, and only when the types match
+    bad = r[:5] + [s[5] + 1 * 10 * 2] + r[6:]                                                   # rank 5 = member 1
+    assert _status(hrs, s, bad, 4, **kw) == gc.GC_ERR_INVALID_ARG                              # bf16 -> fp32
+    bad = r[:5] + [s[5] + 2 * 10 * 2] + r[6:]                                                   # member 2's chunk
+    assert _status(hrs, s, bad, 4, **dict(kw, out_dtype="bf16")) == gc.GC_ERR_INVALID_ARG
+    assert _status(hrs, s, r, 4, **dict(kw, recv_count=0)) == gc.GC_OK

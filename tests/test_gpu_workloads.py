@@ -467,3 +467,63 @@ def test_wire_bf16_ring_error_study():
         print(f"fsdp_layer_n64 {order}: error / mean|x|: median {stats[order + '64'][0]:.3e}, "
               f"p99 {stats[order + '64'][1]:.3e}, max {stats[order + '64'][2]:.3e} ({len(rel)} samples)", flush=True)
     assert stats["ring_wire64"][0] > 10 * stats["ring64"][0] and stats["ring_wire64"][2] > stats["ring64"][2]
+
+
+def test_hier_ar_n16_and_hsdp_layer_full():
+    """Two nodes of eight (AIG6 §6.3.6's HSDP example) at full size: the
+    two-level all-reduce of 16 x 64 MiB bf16 (avg) and the HSDP reduce-scatter
+    of one transformer layer (bf16 -> fp32 avg), sampled against the oracle's
+    two-level fold; every rank's all-reduce result is identical and the shard
+    each group holds is the same."""
+    cfg = WORKLOADS["hier_ar_n16"]
+    N, S, count = cfg["nranks"], cfg["group"], cfg["count"]
+    R = N // S
+    keys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    arena = gc.RankArena(N)
+    send = arena.alloc(count, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(send[r], keys[r], cfg["sigma"])
+    recv = arena.alloc(count, "bf16")
+    gc.gc_hier_all_reduce(send, recv, S, op="avg", order="ring")
+    torch.cuda.synchronize()
+    for r in range(1, N):
+        assert torch.equal(recv[r].view(torch.int16), recv[0].view(torch.int16)), f"rank {r} differs"
+    c1 = -(-count // S)
+    edges = []
+    for i in range(S):
+        lo = i * c1
+        L = min(count, lo + c1) - lo
+        c2 = -(-L // R)
+        for h in range(R):
+            a, b = lo + min(L, h * c2), lo + min(L, (h + 1) * c2)
+            edges += [a, a + 1, b - 2, b - 1]
+    pos = np.unique(np.concatenate([np.random.default_rng(31).integers(0, count, size=1 << 17), edges]))
+    pos = pos[(pos >= 0) & (pos < count)]
+    vals = np.stack([G.normal_bf16(keys[r], pos, cfg["sigma"]) for r in range(N)])
+    g0, m0 = SM.hier_fold_starts(pos, count, S, R, "ring")
+    want = SM.hier_reduce_positions(vals, S, g0, m0, "bf16", "avg", "bf16")
+    assert_same(_gather(recv[5], pos), want, "bf16", "two-level all-reduce")
+    del send, recv
+    torch.cuda.empty_cache()
+
+    numels = [n for _, n in fsdp_layer_tensors()]
+    _, _, Sflat, _ = OB.flat_param_shards(numels, S)
+    rc = Sflat // S
+    arena = gc.RankArena(N)
+    grads = arena.alloc(Sflat, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(grads[r], keys[r], 1e-3)
+    shards = arena.alloc(rc, "fp32")
+    gc.gc_hsdp_reduce_scatter(grads, shards, S, op="avg", order="ring")
+    torch.cuda.synchronize()
+    for i in range(S):
+        for g in range(1, R):
+            assert torch.equal(shards[g * S + i], shards[i]), f"member {i} group {g}"
+    rng = np.random.default_rng(32)
+    for i in (0, 3, S - 1):
+        k = np.unique(np.concatenate([rng.integers(0, rc, size=4096), [0, rc - 1]]))
+        p = i * rc + k
+        vals = np.stack([G.normal_bf16(keys[r], p, 1e-3) for r in range(N)])
+        g0, m0 = SM.hier_fold_starts(p, Sflat, S, R, "ring", chunk=rc)
+        want = SM.hier_reduce_positions(vals, S, g0, m0, "bf16", "avg", "fp32")
+        assert_same(_gather(shards[S + i], k), want, "fp32", f"hsdp member {i}")
