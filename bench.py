@@ -514,7 +514,7 @@ class MoeWorkload(Workload):
             GD.fill_normal_bf16_rows(self.send[s], torch.from_numpy(rows[s]).cuda(), self.H, _keyed(args.seed, s), 1.0)
         total_rows = int(self.splits.sum())
         self.bytes_per_step = 2 * total_rows * self.row_bytes
-        self.dominant = "a2a_kernel"
+        self.dominant = "segment_vec_kernel (all-to-all, one contiguous copy per block)"
         self.dominant_bytes = self.bytes_per_step
         self.frac_dst0 = float(self.splits[:, 0, :].sum() / total_rows)
         self.rows = rows
@@ -532,23 +532,16 @@ class MoeWorkload(Workload):
         import numpy as np
         from gen import host as G
         from oracle import collectives as C
-        # the full routing, with 256-element rows (the first 256 of the 4096 hidden values)
-        h = 256
-        sends = [np.concatenate([G.normal_bf16(_keyed(seed, s), tok * self.H + np.arange(h), 1.0)
-                                 for tok in self.rows[s][:4096]]) for s in range(self.N)]
-        # keep the splits consistent with the truncated row lists: first 4096 rows of each source
-        sub = np.zeros_like(self.splits)
-        for s in range(self.N):
-            left = 4096
-            for d in range(self.N):
-                for e in range(self.splits.shape[2]):
-                    take = min(left, int(self.splits[s, d, e]))
-                    sub[s, d, e] = take
-                    left -= take
+        # the full routing, with 64-element rows (the first 64 of the 4096 hidden values)
+        h = 64
+        cols = np.arange(h, dtype=np.uint64)
+        sends = [G.normal_bf16(_keyed(seed, s), (self.rows[s].astype(np.uint64)[:, None] * np.uint64(self.H)
+                                                 + cols).reshape(-1), 1.0) for s in range(self.N)]
+        sub = self.splits
 
         def run():
             return C.all_to_all(sends, sub, h)
-        return run, 2 * int(sub.sum()) * h * 2, "oracle all-to-all of the first 4096 rows of each source, 256 of 4096 columns"
+        return run, 2 * int(sub.sum()) * h * 2, "oracle all-to-all of every row, 64 of 4096 columns"
 
 
 class MoeEpWorkload(Workload):

@@ -232,7 +232,7 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
   GC_TRY(check_ranks(nranks));
   if (!send || !recv || !splits || experts_per_rank < 1 || row_bytes == 0) return GC_ERR_INVALID_ARG;
   const int N = nranks, E = experts_per_rank;
-  if (static_cast<int64_t>(N) * E > gci::kA2AMaxBlocks) return GC_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(N) * N * E > (int64_t(1) << 24)) return GC_ERR_UNSUPPORTED;
 
   std::vector<int64_t> send_rows(N, 0), recv_rows(N, 0);
   for (int s = 0; s < N; ++s)
@@ -263,24 +263,33 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
     for (int s = 0; s < N; ++s)
       if (overlaps(all[r], span(send[s], send_rows[s] * row_bytes))) return GC_ERR_INVALID_ARG;
 
-  // Destinations are split into groups small enough for one launch each.
-  const int dg = std::max(1, gci::kA2AMaxBlocks / (N * E));
-  std::vector<int32_t> base(N, 0), rows;
-  for (int d0 = 0; d0 < N; d0 += dg) {
-    const int dc = std::min(dg, N - d0);
-    rows.assign(static_cast<size_t>(N) * dc * E, 0);
-    for (int s = 0; s < N; ++s)
-      for (int dl = 0; dl < dc; ++dl)
-        for (int e = 0; e < E; ++e)
-          rows[(static_cast<size_t>(s) * dc + dl) * E + e] =
-              static_cast<int32_t>(splits[(static_cast<int64_t>(s) * N + d0 + dl) * E + e]);
-    gci::A2ACall call{send, recv, N, E, d0, dc, row_bytes, base.data(), rows.data(), stream};
-    GC_TRY(gci::launch_all_to_all(call));
-    for (int s = 0; s < N; ++s)
-      for (int dl = 0; dl < dc; ++dl)
-        for (int e = 0; e < E; ++e) base[s] += rows[(static_cast<size_t>(s) * dc + dl) * E + e];
+  // Every (s, d, e) block is contiguous in send[s] and in recv[d]: the
+  // all-to-all is one contiguous copy per non-empty block, done by the
+  // segment-copy kernel in equal-byte tiles across blocks.
+  std::vector<int64_t> roff(static_cast<size_t>(N) * N * E, 0);
+  for (int d = 0; d < N; ++d) {
+    int64_t run = 0;
+    for (int e = 0; e < E; ++e)
+      for (int s = 0; s < N; ++s) {
+        const size_t b = (static_cast<size_t>(s) * N + d) * E + e;
+        roff[b] = run;
+        run += splits[b];
+      }
   }
-  return GC_OK;
+  std::vector<gci::Segment> segs;
+  for (int s = 0; s < N; ++s) {
+    int64_t run = 0;
+    for (int d = 0; d < N; ++d)
+      for (int e = 0; e < E; ++e) {
+        const size_t b = (static_cast<size_t>(s) * N + d) * E + e;
+        const int64_t v = splits[b];
+        if (v)
+          segs.push_back(gci::Segment{static_cast<const char*>(send[s]) + run * row_bytes,
+                                      static_cast<char*>(recv[d]) + roff[b] * row_bytes, v * row_bytes});
+        run += v;
+      }
+  }
+  return gci::launch_segment_copy(segs.data(), segs.size(), stream);
 }
 
 // ------------------------------------------------------- two-level / HSDP

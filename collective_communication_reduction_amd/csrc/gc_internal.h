@@ -94,24 +94,6 @@ struct Segment {
 
 gc_status launch_segment_copy(const Segment* segs, size_t nseg, hipStream_t stream);
 
-// One all-to-all launch covering destinations [d0, d0 + dcount).
-struct A2ACall {
-  const void* const* send;
-  void* const* recv;
-  int nranks;
-  int experts;
-  int d0;
-  int dcount;
-  uint64_t row_bytes;
-  const int32_t* send_base;  // [nranks] row offset in send[s] where destination d0 starts
-  const int32_t* rows;       // [nranks][dcount][experts] rows of each block
-  hipStream_t stream;
-};
-
-// Largest nranks * dcount * experts one launch can describe.
-constexpr int kA2AMaxBlocks = 512;
-
-gc_status launch_all_to_all(const A2ACall& call);
 
 // MoE routing plan (see gc_moe_route).  Routes of source s are cut into tiles
 // of `tile` routes; counts holds [tiles][nranks * experts_per_rank] int32 and

@@ -1,12 +1,14 @@
-// Pure data-movement kernels for gfx950: the segment copy behind DDP bucket
-// pack / unpack (AIG6 §6.2.4 and NXMR §5.1 gradient buckets; DTLM §4 FSDP1
-// FlatParameter layout) and the all-to-all(v) block permutation of MoE
-// dispatch (DTLM §2 "All-to-All", DTLM §8 All-to-AllV).
+// The segment copy for gfx950: a batch of (source, destination, bytes)
+// copies in one launch.  It carries DDP bucket pack / unpack (AIG6 §6.2.4 and
+// NXMR §5.1 gradient buckets; DTLM §4 FSDP1 FlatParameter layout) and the
+// all-to-all(v) block permutation (DTLM §2 "All-to-All", DTLM §8
+// All-to-AllV), whose (source, destination, expert) blocks are contiguous on
+// both sides, so each block is one segment.
 //
-// Both are HBM streams with no arithmetic.  Work is cut into equal-byte tiles
-// across all segments or rows, so a launch that mixes one huge tensor with
-// many tiny ones, or a skewed all-to-all where most rows go to one rank, still
-// gives every workgroup the same number of bytes.
+// An HBM stream with no arithmetic.  Work is cut into equal-byte tiles across
+// all segments, so a launch that mixes one huge tensor with many tiny ones, or
+// a skewed all-to-all where most rows go to one rank, still gives every
+// workgroup the same number of bytes.
 
 #include <algorithm>
 
@@ -19,7 +21,7 @@ using namespace gcdev;
 
 // ------------------------------------------------------------ segment copy
 
-constexpr int kMaxSeg = 48;
+constexpr int kMaxSeg = 128;  // kernel arguments: 3.6 KiB of the 4 KiB limit
 constexpr int kSegU = 4;                          // 16-byte vectors per thread per tile
 constexpr uint64_t kSegTileVec = kThreads * kSegU;
 
@@ -105,169 +107,12 @@ __global__ void __launch_bounds__(kThreads) segment_narrow_kernel(const SegArgs 
   }
 }
 
-// ------------------------------------------------------------ all-to-all
-
-constexpr int kA2AMax = gci::kA2AMaxBlocks;
-static_assert(2 * kThreads >= kA2AMax, "the block scans hold two entries per thread");
-
-struct A2AArgs {
-  const char* send[GC_MAX_RANKS];
-  char* recv[GC_MAX_RANKS];
-  uint64_t row_bytes;
-  int32_t N, E, d0, Dg;
-  uint32_t rows_per_tile;
-  int32_t send_base[GC_MAX_RANKS];
-  int32_t rows[kA2AMax];  // block (s, dl, e) at (s * Dg + dl) * E + e
-};
-
-// Exclusive prefix sums of up to 512 values held two per thread (elements 2t
-// and 2t+1), across the workgroup.  Returns the prefix of element 2t; *total
-// gets the sum of everything.  Uses wavefront shuffles and one LDS exchange.
-__device__ int32_t scan_pairs(int32_t v0, int32_t v1, int32_t* s_wave, int32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  int32_t x = v0 + v1;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
-  int32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    if (w < wave) before += s_wave[w];
-    all += s_wave[w];
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - (v0 + v1);
-}
-
-template <typename V>
-__device__ __forceinline__ V ld_any(const char* p) {
-  if constexpr (sizeof(V) == 16) return ld16(p);
-  else return *reinterpret_cast<const V*>(p);
-}
-template <typename V>
-__device__ __forceinline__ void st_any(char* p, V v) {
-  if constexpr (sizeof(V) == 16) st16(p, v);
-  else *reinterpret_cast<V*>(p) = v;
-}
-
-// Each workgroup first derives, in LDS, every block's first row in the
-// launch's work order (source-major) and its source and destination row
-// addresses; then it copies whole tiles of rows_per_tile rows, each lane
-// resolving its row's block by binary search.
-template <typename V, int UNR>
-__global__ void __launch_bounds__(kThreads) a2a_kernel(const A2AArgs a) {
-  __shared__ int32_t s_pre[kA2AMax + 1];   // work-order first row of each block
-  __shared__ const char* s_src[kA2AMax];   // address of the block's first row in send[s]
-  __shared__ char* s_dst[kA2AMax];         // address of the block's first row in recv[d]
-  __shared__ int32_t s_rpre[kA2AMax];      // destination-order first row of each block
-  __shared__ int32_t s_wave[kThreads / 64];
-
-  const int nblk = a.N * a.Dg * a.E;
-  const int t2 = 2 * threadIdx.x;
-
-  // Work order (s, dl, e): prefix over rows.
-  {
-    const int32_t v0 = t2 < nblk ? a.rows[t2] : 0;
-    const int32_t v1 = t2 + 1 < nblk ? a.rows[t2 + 1] : 0;
-    int32_t total;
-    const int32_t p = scan_pairs(v0, v1, s_wave, &total);
-    if (t2 < nblk) s_pre[t2] = p;
-    if (t2 + 1 < nblk) s_pre[t2 + 1] = p + v0;
-    if (threadIdx.x == 0) s_pre[nblk] = total;
-  }
-  __syncthreads();
-  // Source rows: blocks of source s are contiguous in send[s], starting at send_base[s].
-  for (int b = threadIdx.x; b < nblk; b += kThreads) {
-    const int s = b / (a.Dg * a.E);
-    const int64_t row = a.send_base[s] + (s_pre[b] - s_pre[s * a.Dg * a.E]);
-    s_src[b] = a.send[s] + row * static_cast<int64_t>(a.row_bytes);
-  }
-  // Destination rows: at rank d0+dl, blocks are laid out by (e, s).
-  {
-    const int NE = a.N * a.E;
-    auto value = [&](int q) -> int32_t {  // q = (dl * E + e) * N + s
-      if (q >= nblk) return 0;
-      const int s = q % a.N;
-      const int de = q / a.N;  // dl * E + e
-      const int dl = de / a.E;
-      const int e = de - dl * a.E;
-      return a.rows[(s * a.Dg + dl) * a.E + e];
-    };
-    const int32_t v0 = value(t2), v1 = value(t2 + 1);
-    int32_t total;
-    const int32_t p = scan_pairs(v0, v1, s_wave, &total);
-    // Each thread holds the prefixes of q = t2 and t2 + 1; the offset within
-    // destination dl subtracts the prefix at q = dl * NE, which another thread
-    // owns, so the exclusive prefixes go through LDS first.
-    if (t2 < nblk) s_rpre[t2] = p;
-    if (t2 + 1 < nblk) s_rpre[t2 + 1] = p + v0;
-    __syncthreads();
-    for (int q = threadIdx.x; q < nblk; q += kThreads) {
-      const int s = q % a.N;
-      const int de = q / a.N;
-      const int dl = de / a.E;
-      const int e = de - dl * a.E;
-      const int64_t row = s_rpre[q] - s_rpre[dl * NE];
-      s_dst[(s * a.Dg + dl) * a.E + e] = a.recv[a.d0 + dl] + row * static_cast<int64_t>(a.row_bytes);
-    }
-  }
-  __syncthreads();
-
-  const int64_t total_rows = s_pre[nblk];
-  const uint64_t vpr = a.row_bytes / sizeof(V);
-  const int64_t ntiles = (total_rows + a.rows_per_tile - 1) / a.rows_per_tile;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t row0 = tile * a.rows_per_tile;
-    const int64_t row1 = min<int64_t>(total_rows, row0 + a.rows_per_tile);
-    const uint64_t nv = static_cast<uint64_t>(row1 - row0) * vpr;
-    for (uint64_t base = 0; base < nv; base += static_cast<uint64_t>(kThreads) * UNR) {
-      V buf[UNR];
-      char* dptr[UNR];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        // Lanes past the tile's end reload its last vector and skip the store.
-        const uint64_t idx = min(base + u * kThreads + threadIdx.x, nv - 1);
-        const int64_t row = row0 + static_cast<int64_t>(idx / vpr);
-        const uint64_t col = idx - static_cast<uint64_t>(row - row0) * vpr;
-        int lo = 0, hi = nblk;  // last block with s_pre[b] <= row (never an empty block)
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_pre[mid] <= row) lo = mid; else hi = mid;
-        }
-        const uint64_t off = static_cast<uint64_t>(row - s_pre[lo]) * a.row_bytes + col * sizeof(V);
-        buf[u] = ld_any<V>(s_src[lo] + off);
-        dptr[u] = s_dst[lo] + off;
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u)
-        if (base + u * kThreads + threadIdx.x < nv) st_any<V>(dptr[u], buf[u]);
-    }
-  }
-}
-
 // ------------------------------------------------------------ host side
 
 #ifndef GC_SEG_MAX_GRID
 #define GC_SEG_MAX_GRID (1u << 20)
 #endif
-#ifndef GC_A2A_MAX_GRID
-#define GC_A2A_MAX_GRID (1u << 20)
-#endif
-#ifndef GC_A2A_TILE_BYTES
-#define GC_A2A_TILE_BYTES 32768
-#endif
-#ifndef GC_A2A_UNR
-#define GC_A2A_UNR 4
-#endif
-
 constexpr uint32_t kMaxGrid = GC_SEG_MAX_GRID;
-constexpr uint32_t kA2AMaxGrid = GC_A2A_MAX_GRID;
 
 template <class K, class A>
 gc_status launch(K kernel, const A& args, uint32_t grid, hipStream_t stream) {
@@ -348,37 +193,6 @@ gc_status launch_segment_copy(const Segment* segs, size_t nseg, hipStream_t stre
     }
   }
   return GC_OK;
-}
-
-gc_status launch_all_to_all(const A2ACall& c) {
-  A2AArgs a{};
-  int64_t total = 0;
-  for (int s = 0; s < c.nranks; ++s) {
-    a.send[s] = static_cast<const char*>(c.send[s]);
-    a.recv[s] = static_cast<char*>(c.recv[s]);
-    a.send_base[s] = c.send_base[s];
-  }
-  const int nblk = c.nranks * c.dcount * c.experts;
-  for (int b = 0; b < nblk; ++b) {
-    a.rows[b] = c.rows[b];
-    total += c.rows[b];
-  }
-  if (total == 0) return GC_OK;
-  a.row_bytes = c.row_bytes;
-  a.N = c.nranks;
-  a.E = c.experts;
-  a.d0 = c.d0;
-  a.Dg = c.dcount;
-  // Fixed payload per tile (GC_A2A_TILE_BYTES, at least one row).
-  a.rows_per_tile = static_cast<uint32_t>(
-      std::max<uint64_t>(1, std::min<uint64_t>(1u << 20, GC_A2A_TILE_BYTES / c.row_bytes)));
-  const int64_t ntiles = (total + a.rows_per_tile - 1) / a.rows_per_tile;
-  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(ntiles, kA2AMaxGrid));
-  uint64_t m = c.row_bytes;
-  for (int s = 0; s < c.nranks; ++s) m |= addr(c.send[s]) | addr(c.recv[s]);
-  if ((m & 15) == 0) return launch(a2a_kernel<u32x4, GC_A2A_UNR>, a, grid, c.stream);
-  if ((m & 3) == 0) return launch(a2a_kernel<uint32_t, 8>, a, grid, c.stream);
-  return launch(a2a_kernel<uint8_t, 8>, a, grid, c.stream);
 }
 
 }  // namespace gci

@@ -135,7 +135,10 @@ gc_status gc_all_reduce(const void* const* send, void* const* recv, size_t count
  *            a block keep their order.  With experts_per_rank == 1 this is
  *            plain all_to_all_v ordered by source.
  *   row_bytes bytes per row (any value >= 1).  Row counts per rank must be
- *            below 2^31.  Pure data movement (bit-exact); buffers must not overlap.
+ *            below 2^31; nranks^2 * experts_per_rank at most 2^24.  Pure data
+ *            movement (bit-exact); buffers must not overlap.  Each non-empty
+ *            block is one contiguous copy; the copies run in equal-byte tiles,
+ *            up to 128 blocks per launch.
  */
 gc_status gc_all_to_all(const void* const* send, void* const* recv, const int64_t* splits,
                         int nranks, int experts_per_rank, size_t row_bytes, hipStream_t stream);

@@ -260,7 +260,8 @@ def _a2a_case(N, E, row_bytes, seed, max_rows=5, zero_frac=0.2):
 
 
 @pytest.mark.parametrize("N,E,row_bytes", [(2, 1, 16), (3, 2, 48), (4, 1, 6), (8, 8, 8192), (8, 8, 16),
-                                           (5, 3, 1), (16, 8, 32), (8, 1, 4100)])
+                                           (5, 3, 1), (16, 8, 32), (8, 1, 4100),
+                                           (64, 16, 32), (64, 1, 2)])   # 65,536 blocks: many launches
 def test_all_to_all(N, E, row_bytes):
     splits, sends = _a2a_case(N, E, row_bytes, seed=N * E + row_bytes)
     want = C.all_to_all(sends, splits, row_bytes)
