@@ -515,7 +515,9 @@ gc_status moe_route_geom(const int64_t* ntokens, int nranks, int topk, int E, Mo
   if (!ntokens || topk < 1 || E < 1) return GC_ERR_INVALID_ARG;
   if (topk > kMoeMaxTopk || static_cast<int64_t>(nranks) * E > kMoeMaxBins) return GC_ERR_UNSUPPORTED;
   const int64_t nbins = static_cast<int64_t>(nranks) * E;
-  g.tile = static_cast<int32_t>(std::max<int64_t>(512, (nbins + 63) / 64 * 64));
+  // Tiles of kMoeRouteTile routes (four wavefronts) while the experts fit;
+  // beyond, one wavefront per tile of at least one route per expert.
+  g.tile = static_cast<int32_t>(std::max<int64_t>(gci::kMoeRouteTile, (nbins + 63) / 64 * 64));
   for (int s = 0; s < nranks; ++s) {
     if (ntokens[s] < 0) return GC_ERR_INVALID_ARG;
     if (ntokens[s] >= (int64_t(1) << 31)) return GC_ERR_UNSUPPORTED;

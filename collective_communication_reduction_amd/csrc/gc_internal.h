@@ -128,6 +128,12 @@ struct MoeMoveCall {
   hipStream_t stream;
 };
 
+// Routes per routing-plan tile while the experts fit it (four wavefronts).
+#ifndef GC_MOE_ROUTE_TILE
+#define GC_MOE_ROUTE_TILE 1024
+#endif
+constexpr int32_t kMoeRouteTile = GC_MOE_ROUTE_TILE;
+
 gc_status launch_moe_route(const MoeRouteCall& call);
 gc_status launch_moe_dispatch(const MoeMoveCall& call);
 gc_status launch_moe_combine(const MoeMoveCall& call);

@@ -6,8 +6,9 @@
 //             ids to the split table and, per (token, k), the rank and row its
 //             copy occupies in the receive layout (by local expert, then
 //             source, then token).  Three small kernels: a stable in-tile rank
-//             per route (one wavefront per tile, ballot-grouped by expert), a
-//             per-destination scan of the tile counts, and the final row sums.
+//             per route (lanes matched by expert with one ballot per id bit),
+//             a per-destination scan of the tile totals, and the final rows
+//             (each tile adds the counts of the source's earlier tiles).
 //   dispatch  the pack fused into the all-to-all: each token row is read once
 //             and written to its K destinations (an HBM stream, no arithmetic).
 //   combine   the inverse all-to-all fused with the weighted un-permute: each
@@ -42,6 +43,7 @@ struct RouteArgs {
   int64_t* splits;            // [N][N][E]
   int32_t tile;               // routes per tile
   int32_t N, E, nbins;
+  int32_t nbits;              // bits of the largest expert id, nbins - 1
 };
 
 template <int P>
@@ -51,10 +53,83 @@ __device__ __forceinline__ int source_of(const int32_t (&first)[P + 1], int N, i
   return s;
 }
 
-// One wavefront per tile: the rank of every route among the tile's earlier
-// routes to the same expert, grouping lanes that share an expert by ballot.
+// Rank of each route of one 64-route chunk among the earlier routes to the
+// same expert.  Each lane finds the lanes holding its expert with one ballot
+// per bit of the expert id (nbits ballots, however many experts the chunk
+// holds); its rank is the running count `cnt` (LDS) plus the matching lanes
+// below it, and the lowest lane of each group advances the count.  Within a
+// wavefront the LDS read completes before the write is issued.
+__device__ __forceinline__ int32_t rank_in_chunk(int32_t g, bool valid, int32_t* cnt, int lane, int nbits) {
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  uint64_t same = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = (g >> bit) & 1;
+    const uint64_t b = __ballot(set);
+    same &= set ? b : ~b;
+  }
+  const int32_t base = cnt[valid ? g : 0];
+  if (!valid) return -1;
+  const uint64_t mine = same & below;
+  if (mine == 0) cnt[g] = base + __popcll(same);
+  return base + __popcll(mine);
+}
+
+// Tiles of kMoeRouteTile routes while the experts fit the tile: each of the
+// four wavefronts ranks its share of the routes with the expert ids of all its
+// chunks loaded up front, then the wavefronts' per-expert counts are scanned in LDS and each
+// rank is offset by the counts of the wavefronts before it.  Writes (expert,
+// rank in tile) per route and the tile's count per expert.
+constexpr int kRouteWaves = 4;
+constexpr int kRouteChunks = gci::kMoeRouteTile / (kRouteWaves * kWave);  // 64-route chunks per wavefront
+static_assert(kRouteChunks * kRouteWaves * kWave == gci::kMoeRouteTile, "tile = whole chunks per wavefront");
+
 template <int P>
-__global__ void __launch_bounds__(kWave) route_count_kernel(const RouteArgs<P> a) {
+__global__ void __launch_bounds__(kWave * kRouteWaves) route_count_kernel(const RouteArgs<P> a) {
+  extern __shared__ int32_t cnt[];  // [kRouteWaves][nbins]
+  const int32_t b = blockIdx.x;
+  const int s = source_of<P>(a.tile0, a.N, b);
+  const int64_t lo = static_cast<int64_t>(b - a.tile0[s]) * a.tile;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t wlo = lo + static_cast<int64_t>(w) * kWave * kRouteChunks;
+  const int64_t n = max<int64_t>(0, min<int64_t>(kWave * kRouteChunks, a.routes[s] - wlo));
+  for (int i = threadIdx.x; i < kRouteWaves * a.nbins; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  int32_t g[kRouteChunks], rank[kRouteChunks];
+#pragma unroll
+  for (int c = 0; c < kRouteChunks; ++c) {
+    const int64_t i = c * kWave + lane;
+    g[c] = i < n ? a.experts[s][wlo + i] : -1;
+  }
+#pragma unroll
+  for (int c = 0; c < kRouteChunks; ++c) {
+    const bool valid = g[c] >= 0 && g[c] < a.nbins;
+    rank[c] = rank_in_chunk(g[c], valid, cnt + w * a.nbins, lane, a.nbits);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.nbins; e += blockDim.x) {
+    int32_t run = 0;
+    for (int q = 0; q < kRouteWaves; ++q) {
+      const int32_t v = cnt[q * a.nbins + e];
+      cnt[q * a.nbins + e] = run;
+      run += v;
+    }
+    a.counts[static_cast<int64_t>(b) * a.nbins + e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kRouteChunks; ++c) {
+    const int64_t i = c * kWave + lane;
+    if (i >= n) continue;
+    const bool valid = g[c] >= 0 && g[c] < a.nbins;
+    const int32_t before = cnt[w * a.nbins + (valid ? g[c] : 0)];  // routes of earlier wavefronts
+    a.dest[s][wlo + i] = valid ? make_int2(g[c], rank[c] + before) : make_int2(-1, -1);
+  }
+}
+
+// More experts than kMoeRouteTile: one wavefront per tile of a.tile routes
+// (at least one route per expert), chunk by chunk.
+template <int P>
+__global__ void __launch_bounds__(kWave) route_count_wide_kernel(const RouteArgs<P> a) {
   extern __shared__ int32_t cnt[];
   const int32_t b = blockIdx.x;
   const int s = source_of<P>(a.tile0, a.N, b);
@@ -63,23 +138,12 @@ __global__ void __launch_bounds__(kWave) route_count_kernel(const RouteArgs<P> a
   const int lane = threadIdx.x;
   for (int i = lane; i < a.nbins; i += kWave) cnt[i] = 0;
   __syncthreads();
-  const uint64_t below = (uint64_t(1) << lane) - 1;
   for (int64_t c0 = 0; c0 < n; c0 += kWave) {
     const int64_t i = c0 + lane;
     const bool in = i < n;
     const int32_t g = in ? a.experts[s][lo + i] : -1;
     const bool valid = in && g >= 0 && g < a.nbins;
-    uint64_t pending = __ballot(valid);
-    int32_t rank = -1;
-    while (pending) {
-      const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
-      const int32_t v = __shfl(g, leader);
-      const uint64_t same = __ballot(valid && g == v);
-      const int32_t base = cnt[v];
-      if (valid && g == v) rank = base + __popcll(same & below);
-      if (lane == leader) cnt[v] = base + __popcll(same);
-      pending &= ~same;
-    }
+    const int32_t rank = rank_in_chunk(g, valid, cnt, lane, a.nbits);
     if (in) a.dest[s][lo + i] = valid ? make_int2(g, rank) : make_int2(-1, -1);
   }
   __syncthreads();
@@ -109,9 +173,21 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* lds,
   return off + x - v;
 }
 
-// One workgroup per destination d: per (source, local expert) the tile
-// counts become exclusive prefixes and their total the split; the receive
-// offsets follow by scanning the blocks in (expert, source) order.
+// Sum of counts[t][g] over tiles [t0, t1): independent loads, eight in flight.
+__device__ __forceinline__ int32_t sum_tiles(const int32_t* counts, int32_t nbins, int32_t g, int32_t t0, int32_t t1) {
+  int32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int32_t t = t0;
+  for (; t + 8 <= t1; t += 8) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += counts[static_cast<int64_t>(t + k) * nbins + g];
+  }
+  for (; t < t1; ++t) acc[0] += counts[static_cast<int64_t>(t) * nbins + g];  // integer sums: any order
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+// One workgroup per destination d: each (source, local expert) block's total
+// over the tiles is its split; the receive offsets follow by scanning the
+// blocks in (expert, source) order.
 template <int P>
 __global__ void __launch_bounds__(kThreads) route_scan_kernel(const RouteArgs<P> a) {
   __shared__ int32_t lds[kThreads / kWave];
@@ -126,12 +202,7 @@ __global__ void __launch_bounds__(kThreads) route_scan_kernel(const RouteArgs<P>
       const int e = i / a.N;
       s = i - e * a.N;
       g = d * a.E + e;
-      for (int32_t t = a.tile0[s]; t < a.tile0[s + 1]; ++t) {
-        int32_t* c = a.counts + static_cast<int64_t>(t) * a.nbins + g;
-        const int32_t v = *c;
-        *c = total;
-        total += v;
-      }
+      total = sum_tiles(a.counts, a.nbins, g, a.tile0[s], a.tile0[s + 1]);
       a.splits[(static_cast<int64_t>(s) * a.N + d) * a.E + e] = total;
     }
     int32_t sum;
@@ -141,18 +212,23 @@ __global__ void __launch_bounds__(kThreads) route_scan_kernel(const RouteArgs<P>
   }
 }
 
+// One workgroup per tile: the first receive row of each expert's routes in
+// this tile (block offset plus the counts of the source's earlier tiles),
+// then row = that + rank in tile, rank = expert / E.
 template <int P>
 __global__ void __launch_bounds__(kThreads) route_final_kernel(const RouteArgs<P> a) {
+  extern __shared__ int32_t first_row[];  // [nbins]
   const int32_t b = blockIdx.x;
   const int s = source_of<P>(a.tile0, a.N, b);
+  for (int g = threadIdx.x; g < a.nbins; g += kThreads)
+    first_row[g] = a.roff[static_cast<int64_t>(s) * a.nbins + g] + sum_tiles(a.counts, a.nbins, g, a.tile0[s], b);
+  __syncthreads();
   const int64_t lo = static_cast<int64_t>(b - a.tile0[s]) * a.tile;
   const int64_t n = min<int64_t>(a.tile, a.routes[s] - lo);
   for (int64_t i = threadIdx.x; i < n; i += kThreads) {
     const int2 p = a.dest[s][lo + i];
     if (p.x < 0) continue;
-    const int32_t row = a.roff[static_cast<int64_t>(s) * a.nbins + p.x] +
-                        a.counts[static_cast<int64_t>(b) * a.nbins + p.x] + p.y;
-    a.dest[s][lo + i] = make_int2(p.x / a.E, row);
+    a.dest[s][lo + i] = make_int2(p.x / a.E, first_row[p.x] + p.y);
   }
 }
 
@@ -388,14 +464,19 @@ gc_status route_impl(const gci::MoeRouteCall& c) {
   a.N = c.nranks;
   a.E = c.experts_per_rank;
   a.nbins = c.nranks * c.experts_per_rank;
+  a.nbits = 0;
+  while ((1 << a.nbits) < a.nbins) ++a.nbits;
   const size_t lds = static_cast<size_t>(a.nbins) * sizeof(int32_t);
+  const bool wide = a.tile != kRouteWaves * kRouteChunks * kWave;
   if (tiles > 0) {
-    const gc_status st = launch(route_count_kernel<P>, a, tiles, kWave, lds, c.stream);
+    const gc_status st = wide ? launch(route_count_wide_kernel<P>, a, tiles, kWave, lds, c.stream)
+                              : launch(route_count_kernel<P>, a, tiles, kWave * kRouteWaves, kRouteWaves * lds,
+                                       c.stream);
     if (st != GC_OK) return st;
   }
   gc_status st = launch(route_scan_kernel<P>, a, c.nranks, kThreads, 0, c.stream);
   if (st != GC_OK || tiles == 0) return st;
-  return launch(route_final_kernel<P>, a, tiles, kThreads, 0, c.stream);
+  return launch(route_final_kernel<P>, a, tiles, kThreads, lds, c.stream);
 }
 
 template <class T, int P>

@@ -220,7 +220,7 @@ gc_status gc_fsdp2_all_gather(const void* const* shards, void* const* params, co
 
 /*
  * Scratch bytes gc_moe_route needs, nbins = nranks * E: each source's routes
- * are cut into tiles of max(512, nbins rounded up to 64) routes, and the
+ * are cut into tiles of max(1024, nbins rounded up to 64) routes, and the
  * plan keeps one int32 per tile and global expert, plus nranks * nbins int32.
  */
 size_t gc_moe_route_scratch_bytes(const int64_t* ntokens, int nranks, int topk, int experts_per_rank);

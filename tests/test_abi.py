@@ -188,7 +188,7 @@ def test_moe_route_validation():
     route = gc.gc_moe_route
     nt = [100, 0, 37]
     need = gc.gc_moe_route_scratch_bytes(nt, 2, 4)
-    # tiles of 512 routes: 1 + 0 + 1 tiles x 12 experts, then 3 x 12 offsets, each 256-aligned
+    # tiles of 1024 routes: 1 + 0 + 1 tiles x 12 experts, then 3 x 12 offsets, each 256-aligned
     assert need == 256 + 256
     assert gc.gc_moe_route_scratch_bytes(nt, 9, 4) == 0                     # topk > 8
     assert gc.gc_moe_route_scratch_bytes([1] * 64, 1, 129) == 0              # 64 * 129 experts > 8192
