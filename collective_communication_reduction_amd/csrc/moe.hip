@@ -236,7 +236,13 @@ __global__ void __launch_bounds__(kThreads) route_final_kernel(const RouteArgs<P
 //
 // Rows are cut into units (a 16-byte vector, or one element / byte when the
 // rows or buffers are not 16-byte aligned).  S = 2^lanes_log2 lanes work on a
-// row, two units per lane per step; a workgroup holds kThreads / S rows.
+// row, kMoeU units per lane per step (all loads of a step issued before the
+// first store); a workgroup holds kThreads / S rows.
+
+#ifndef GC_MOE_UNITS
+#define GC_MOE_UNITS 4
+#endif
+constexpr int kMoeU = GC_MOE_UNITS;
 
 template <int P>
 struct DispatchArgs {
@@ -282,15 +288,21 @@ __global__ void __launch_bounds__(kThreads) dispatch_kernel(const DispatchArgs<P
     if (t >= a.ntok[s]) continue;
     const T* src = reinterpret_cast<const T*>(a.tok[s]) + static_cast<uint64_t>(t) * a.R;
     const int2* dst = a.dest[s] + t * a.K;
-    for (uint64_t c = lane; c < a.R; c += 2 * S) {
-      const bool two = c + S < a.R;
-      const T v0 = ld_unit(src + c);
-      const T v1 = ld_unit(src + (two ? c + S : c));  // clamped: no exec-masked load
+    for (uint64_t c = lane; c < a.R; c += kMoeU * S) {
+      T v[kMoeU];
+#pragma unroll
+      for (int j = 0; j < kMoeU; ++j) {
+        const uint64_t cj = c + static_cast<uint64_t>(j) * S;
+        v[j] = ld_unit(src + (cj < a.R ? cj : c));  // clamped: no exec-masked load
+      }
       for (int k = 0; k < a.K; ++k) {
         T* out = route_row<T, P>(a.recv, a.recv_rows, a.N, dst[k], a.R);
         if (!out) continue;
-        st_unit(out + c, v0);
-        if (two) st_unit(out + c + S, v1);
+#pragma unroll
+        for (int j = 0; j < kMoeU; ++j) {
+          const uint64_t cj = c + static_cast<uint64_t>(j) * S;
+          if (j == 0 || cj < a.R) st_unit(out + cj, v[j]);
+        }
       }
     }
   }
@@ -372,13 +384,17 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const CombineArgs<P> 
     const int2* routes = a.dest[s] + t * K;
     const float* wt = a.w[s] + t * K;
     T* out = reinterpret_cast<T*>(a.out[s]) + static_cast<uint64_t>(t) * a.R;
-    for (uint64_t c = lane; c < a.R; c += 2 * S) {
-      const bool two = c + S < a.R;
-      const uint64_t c1 = two ? c + S : c;
-      float acc0[VE], acc1[VE];
+    for (uint64_t c = lane; c < a.R; c += kMoeU * S) {
+      uint64_t cu[kMoeU];
+#pragma unroll
+      for (int u = 0; u < kMoeU; ++u) {
+        const uint64_t cj = c + static_cast<uint64_t>(u) * S;
+        cu[u] = cj < a.R ? cj : c;  // clamped: no exec-masked load
+      }
+      float acc[kMoeU][VE];
       bool any = false;
       for (int k0 = 0; k0 < K; k0 += KB) {
-        T v0[KB], v1[KB];
+        T v[KB][kMoeU];
         bool ok[KB];
         float wk[KB];
 #pragma unroll
@@ -387,27 +403,33 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const CombineArgs<P> 
           ok[j] = row != nullptr;
           wk[j] = wt[k0 + j];
           if (ok[j]) {
-            v0[j] = ld_unit(row + c);
-            v1[j] = ld_unit(row + c1);
+#pragma unroll
+            for (int u = 0; u < kMoeU; ++u) v[j][u] = ld_unit(row + cu[u]);
           }
         }
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
           if (!ok[j]) continue;
-          float y0[VE], y1[VE];
-          U::widen(v0[j], y0);
-          U::widen(v1[j], y1);
-          accumulate(acc0, y0, wk[j], !any);
-          accumulate(acc1, y1, wk[j], !any);
+#pragma unroll
+          for (int u = 0; u < kMoeU; ++u) {
+            float y[VE];
+            U::widen(v[j][u], y);
+            accumulate(acc[u], y, wk[j], !any);
+          }
           any = true;
         }
       }
       if (!any) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc0[e] = acc1[e] = 0.0f;
+        for (int u = 0; u < kMoeU; ++u)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[u][e] = 0.0f;
       }
-      st_unit(out + c, U::narrow(acc0));
-      if (two) st_unit(out + c + S, U::narrow(acc1));
+#pragma unroll
+      for (int u = 0; u < kMoeU; ++u) {
+        const uint64_t cj = c + static_cast<uint64_t>(u) * S;
+        if (u == 0 || cj < a.R) st_unit(out + cj, U::narrow(acc[u]));
+      }
     }
   }
 }
@@ -427,10 +449,10 @@ gc_status launch(Kern kernel, const A& args, uint32_t grid, uint32_t threads, si
 
 uint64_t addr(const void* p) { return reinterpret_cast<uint64_t>(p); }
 
-// Lanes per row: half the row's units rounded up to a power of two, 1..kThreads.
+// Lanes per row: the row's units over kMoeU, rounded up to a power of two, 1..kThreads.
 int lanes_log2_for(uint64_t R) {
   int l = 0;
-  while (l < 8 && (uint64_t(1) << (l + 1)) < R) ++l;
+  while (l < 8 && (uint64_t(1) << l) * kMoeU < R) ++l;
   return l;
 }
 
