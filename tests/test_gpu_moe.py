@@ -217,3 +217,30 @@ def test_malformed_plan_entries_are_skipped():
     assert np.array_equal(o0[1], 0.5 * np.arange(H + 1, 2 * H + 1))
     assert np.all(o0[2] == 0.0) and not np.signbit(o0[2]).any()       # no route kept: zeros
     assert np.array_equal(out[1].cpu().numpy(), r1[0] + r0[1])
+
+
+@pytest.mark.parametrize("N,E,K,H,dtype", [(64, 2, 2, 96, "bf16"), (64, 1, 3, 5, "fp32"), (16, 4, 8, 1, "bf16")])
+def test_many_ranks_round_trip(N, E, K, H, dtype):
+    """The 64-rank argument layout, three and eight routes per token, and rows
+    of one element."""
+    rng = np.random.default_rng(N * K + H)
+    T = [int(x) for x in rng.integers(0, 40, size=N)]
+    experts = _routing(rng, N, E, T, K, drop=0.05)
+    ntok, splits, dest = route_on_device(experts, N, E, K)
+    want_splits = check_plan(experts, N, E, K, splits, dest)
+    rows = [int(r) for r in want_splits.sum(axis=(0, 2))]
+    tokens = [_expert_rows(rng, t, H, dtype, special=False) for t in T]
+    w = [rng.normal(size=(t, K)).astype(np.float32) for t in T]
+    want = M.combine(M.dispatch(tokens, experts, N, E, H), experts, w, N, E, H, dtype)
+    tok_dev = [to_dev(t, dtype) if t.size else 0 for t in tokens]
+    es = 2 if dtype == "bf16" else 4
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    recv = [torch.empty(max(1, r * H), dtype=tdt, device=DEV) for r in rows]
+    gc.gc_moe_dispatch(tok_dev, ntok, dest, K, H * es, recv, rows)
+    out = [torch.empty(max(1, t * H), dtype=tdt, device=DEV) for t in T]
+    w_dev = [torch.from_numpy(x.reshape(-1)).to(DEV) if x.size else 0 for x in w]
+    gc.gc_moe_combine(recv, rows, dest, w_dev, ntok, K, H, dtype, out)
+    torch.cuda.synchronize()
+    for s in range(N):
+        if T[s]:
+            assert_same(from_dev(out[s])[:T[s] * H], want[s], dtype, f"source {s}")
