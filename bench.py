@@ -65,6 +65,7 @@ def parse():
     p.add_argument("--stagger", type=int, default=4096, help="extra bytes between consecutive ranks' memory")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-copy-ceiling", action="store_true", help="skip the 2 GiB copy-ceiling measurement")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="also launch a plain device copy of this many MiB (counter calibration runs)")
     return p.parse_args()
@@ -664,20 +665,62 @@ def make(args):
 
 # ----------------------------------------------------------------- timing
 
-def time_steps(fn, steps, warmup):
-    """HIP events on torch's current stream (the stream every libgc launch uses)."""
+def time_steps(fn, steps, warmup, per_step=None):
+    """HIP events on torch's current stream (the stream every libgc launch uses).
+    Returns ms per step over the whole timed region; with per_step (a list), also
+    appends each step's own event time."""
     import torch
     for k in range(warmup):
         fn(k)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)] if per_step is not None else None
     start.record()
     for k in range(steps):
         fn(warmup + k)
+        if marks:
+            marks[k].record()
     stop.record()
     torch.cuda.synchronize()
+    if marks:
+        prev = start
+        for m in marks:
+            per_step.append(prev.elapsed_time(m))
+            prev = m
     return start.elapsed_time(stop) / steps  # ms per step
+
+
+def copy_ceiling(nbytes=2 << 30, steps=10):
+    """A plain 16-byte copy of nbytes through libgc's segment-copy kernel (a
+    one-rank, one-block all-to-all): read + write bytes per second, GB/s."""
+    import torch
+    import collective_communication_reduction_amd as gc
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    splits = [[[1]]]
+
+    def run(_k):
+        gc.gc_all_to_all([a], [b], splits, nbytes)
+    ms = time_steps(run, steps, 2)
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def host_cpu():
+    """CPU model name and the number of hardware threads of this host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
 
 
 def cpu_baseline(w, seed):
@@ -691,8 +734,20 @@ def cpu_baseline(w, seed):
         if time.perf_counter() - t0 >= 10.0 or reps >= 20:
             break
     per = (time.perf_counter() - t0) / reps
+    model, threads = host_cpu()
     return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}; {reps} runs, {per:.3f} s each, single-threaded numpy"}
+            "sample": f"{what}; {reps} runs, {per:.3f} s each, single-threaded numpy",
+            "host_cpu": model, "host_threads": threads}
+
+
+def _quantile(xs, q):
+    ys = sorted(xs)
+    if not ys:
+        return 0.0
+    k = (len(ys) - 1) * q
+    lo = int(k)
+    hi = min(lo + 1, len(ys) - 1)
+    return ys[lo] + (ys[hi] - ys[lo]) * (k - lo)
 
 
 def main():
@@ -711,7 +766,8 @@ def main():
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
-    ms = time_steps(w.step, args.steps, args.warmup)
+    step_ms = []
+    ms = time_steps(w.step, args.steps, args.warmup, step_ms)
     if type(w).dominant_launch is Workload.dominant_launch:
         kms = ms
         launches = 1
@@ -739,7 +795,14 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": w.dominant, "algorithmic_bytes_per_launch": w.dominant_bytes},
         "bytes_per_step": w.bytes_per_step,
+        "step_ms": {"median": round(_quantile(step_ms, 0.5), 5), "min": round(min(step_ms), 5),
+                    "p90": round(_quantile(step_ms, 0.9), 5)},
     }
+    if not args.no_copy_ceiling:
+        ceiling = copy_ceiling()
+        out["copy_ceiling"] = {"value": round(ceiling, 2), "unit": "GB/s",
+                               "kernel": "segment_vec_kernel, one 2 GiB block (16-byte loads and stores)",
+                               "frac": round(achieved / ceiling, 4)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.seed)
     else:

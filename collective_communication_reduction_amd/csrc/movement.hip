@@ -22,7 +22,10 @@ using namespace gcdev;
 // ------------------------------------------------------------ segment copy
 
 constexpr int kMaxSeg = 128;  // kernel arguments: 3.6 KiB of the 4 KiB limit
-constexpr int kSegU = 4;                          // 16-byte vectors per thread per tile
+#ifndef GC_SEG_U
+#define GC_SEG_U 1
+#endif
+constexpr int kSegU = GC_SEG_U;                   // 16-byte vectors per thread per tile
 constexpr uint64_t kSegTileVec = kThreads * kSegU;
 
 struct SegArgs {
