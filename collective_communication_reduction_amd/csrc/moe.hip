@@ -254,6 +254,7 @@ struct DispatchArgs {
   int32_t grp0[P + 1];     // first row group of each source
   uint64_t R;              // units per row
   int32_t N, K, lanes_log2;
+  int32_t cb;              // column blocks per row (workgroups sharing one row)
 };
 
 template <class T>
@@ -282,18 +283,22 @@ __global__ void __launch_bounds__(kThreads) dispatch_kernel(const DispatchArgs<P
   const int sub = threadIdx.x >> a.lanes_log2, lane = threadIdx.x & (S - 1);
   const int G = kThreads >> a.lanes_log2;
   const int32_t ngroups = a.grp0[a.N];
+  const uint64_t span = static_cast<uint64_t>(kMoeU) * S;  // units a row group covers per step
   for (int32_t b = blockIdx.x; b < ngroups; b += gridDim.x) {
     const int s = source_of<P>(a.grp0, a.N, b);
-    const int64_t t = static_cast<int64_t>(b - a.grp0[s]) * G + sub;
+    const int32_t local = b - a.grp0[s];
+    const int64_t t = static_cast<int64_t>(local / a.cb) * G + sub;
     if (t >= a.ntok[s]) continue;
+    const uint64_t cbeg = static_cast<uint64_t>(local % a.cb) * span;
+    const uint64_t cend = a.cb > 1 ? min(a.R, cbeg + span) : a.R;
     const T* src = reinterpret_cast<const T*>(a.tok[s]) + static_cast<uint64_t>(t) * a.R;
     const int2* dst = a.dest[s] + t * a.K;
-    for (uint64_t c = lane; c < a.R; c += kMoeU * S) {
+    for (uint64_t c = cbeg + lane; c < cend; c += span) {
       T v[kMoeU];
 #pragma unroll
       for (int j = 0; j < kMoeU; ++j) {
         const uint64_t cj = c + static_cast<uint64_t>(j) * S;
-        v[j] = ld_unit(src + (cj < a.R ? cj : c));  // clamped: no exec-masked load
+        v[j] = ld_unit(src + (cj < cend ? cj : c));  // clamped: no exec-masked load
       }
       for (int k = 0; k < a.K; ++k) {
         T* out = route_row<T, P>(a.recv, a.recv_rows, a.N, dst[k], a.R);
@@ -301,7 +306,7 @@ __global__ void __launch_bounds__(kThreads) dispatch_kernel(const DispatchArgs<P
 #pragma unroll
         for (int j = 0; j < kMoeU; ++j) {
           const uint64_t cj = c + static_cast<uint64_t>(j) * S;
-          if (j == 0 || cj < a.R) st_unit(out + cj, v[j]);
+          if (j == 0 || cj < cend) st_unit(out + cj, v[j]);
         }
       }
     }
@@ -319,6 +324,7 @@ struct CombineArgs {
   int32_t grp0[P + 1];
   uint64_t R;
   int32_t N, K, lanes_log2;
+  int32_t cb;
 };
 
 // One unit of K weighted rows: 16-byte vectors of In::VE elements, or single elements.
@@ -377,19 +383,23 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const CombineArgs<P> 
   const int sub = threadIdx.x >> a.lanes_log2, lane = threadIdx.x & (S - 1);
   const int G = kThreads >> a.lanes_log2;
   const int32_t ngroups = a.grp0[a.N];
+  const uint64_t span = static_cast<uint64_t>(kMoeU) * S;
   for (int32_t b = blockIdx.x; b < ngroups; b += gridDim.x) {
     const int s = source_of<P>(a.grp0, a.N, b);
-    const int64_t t = static_cast<int64_t>(b - a.grp0[s]) * G + sub;
+    const int32_t local = b - a.grp0[s];
+    const int64_t t = static_cast<int64_t>(local / a.cb) * G + sub;
     if (t >= a.ntok[s]) continue;
+    const uint64_t cbeg = static_cast<uint64_t>(local % a.cb) * span;
+    const uint64_t cend = a.cb > 1 ? min(a.R, cbeg + span) : a.R;
     const int2* routes = a.dest[s] + t * K;
     const float* wt = a.w[s] + t * K;
     T* out = reinterpret_cast<T*>(a.out[s]) + static_cast<uint64_t>(t) * a.R;
-    for (uint64_t c = lane; c < a.R; c += kMoeU * S) {
+    for (uint64_t c = cbeg + lane; c < cend; c += span) {
       uint64_t cu[kMoeU];
 #pragma unroll
       for (int u = 0; u < kMoeU; ++u) {
         const uint64_t cj = c + static_cast<uint64_t>(u) * S;
-        cu[u] = cj < a.R ? cj : c;  // clamped: no exec-masked load
+        cu[u] = cj < cend ? cj : c;  // clamped: no exec-masked load
       }
       float acc[kMoeU][VE];
       bool any = false;
@@ -428,7 +438,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const CombineArgs<P> 
 #pragma unroll
       for (int u = 0; u < kMoeU; ++u) {
         const uint64_t cj = c + static_cast<uint64_t>(u) * S;
-        if (u == 0 || cj < a.R) st_unit(out + cj, U::narrow(acc[u]));
+        if (u == 0 || cj < cend) st_unit(out + cj, U::narrow(acc[u]));
       }
     }
   }
@@ -456,13 +466,27 @@ int lanes_log2_for(uint64_t R) {
   return l;
 }
 
+// Column blocks per row: rows longer than one workgroup step are shared by
+// several workgroups (each writes a few KiB per row), shorter ones are not.
+#ifndef GC_MOE_SPLIT_ROWS
+#define GC_MOE_SPLIT_ROWS 1
+#endif
+int32_t column_blocks(uint64_t R, int lanes_log2, const int64_t* tokens, int N) {
+  const uint64_t span = static_cast<uint64_t>(kMoeU) << lanes_log2;
+  if (!GC_MOE_SPLIT_ROWS || lanes_log2 < 8 || R <= span) return 1;
+  const uint64_t cb = (R + span - 1) / span;
+  uint64_t groups = 0;  // one row per group here (a full workgroup per row)
+  for (int s = 0; s < N; ++s) groups += static_cast<uint64_t>(tokens[s]) * cb;
+  return groups < (uint64_t(1) << 31) ? static_cast<int32_t>(cb) : 1;  // group indices are int32
+}
+
 template <int P>
-void fill_groups(int32_t (&grp0)[P + 1], int64_t (&ntok)[P], const int64_t* tokens, int N, int G) {
+void fill_groups(int32_t (&grp0)[P + 1], int64_t (&ntok)[P], const int64_t* tokens, int N, int G, int32_t cb) {
   int64_t run = 0;
   for (int s = 0; s < N; ++s) {
     grp0[s] = static_cast<int32_t>(run);
     ntok[s] = tokens[s];
-    run += (tokens[s] + G - 1) / G;
+    run += (tokens[s] + G - 1) / G * cb;
   }
   for (int s = N; s <= P; ++s) grp0[s] = static_cast<int32_t>(run);
 }
@@ -514,7 +538,8 @@ gc_status dispatch_impl(const gci::MoeMoveCall& c, uint64_t R) {
   a.N = c.nranks;
   a.K = c.topk;
   a.lanes_log2 = lanes_log2_for(R);
-  fill_groups<P>(a.grp0, a.ntok, c.tokens, c.nranks, kThreads >> a.lanes_log2);
+  a.cb = column_blocks(R, a.lanes_log2, c.tokens, c.nranks);
+  fill_groups<P>(a.grp0, a.ntok, c.tokens, c.nranks, kThreads >> a.lanes_log2, a.cb);
   if (a.grp0[c.nranks] == 0) return GC_OK;
   const uint32_t grid = std::min<uint32_t>(a.grp0[c.nranks], GC_MOE_MAX_GRID);
   return launch(dispatch_kernel<T, P>, a, grid, kThreads, 0, c.stream);
@@ -534,7 +559,8 @@ gc_status combine_impl(const gci::MoeMoveCall& c, uint64_t R) {
   a.N = c.nranks;
   a.K = c.topk;
   a.lanes_log2 = lanes_log2_for(R);
-  fill_groups<P>(a.grp0, a.ntok, c.tokens, c.nranks, kThreads >> a.lanes_log2);
+  a.cb = column_blocks(R, a.lanes_log2, c.tokens, c.nranks);
+  fill_groups<P>(a.grp0, a.ntok, c.tokens, c.nranks, kThreads >> a.lanes_log2, a.cb);
   if (a.grp0[c.nranks] == 0) return GC_OK;
   const uint32_t grid = std::min<uint32_t>(a.grp0[c.nranks], GC_MOE_MAX_GRID);
   switch (c.topk) {

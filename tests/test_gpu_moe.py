@@ -144,6 +144,7 @@ COMBINE_CASES = [
     ("fp32", 999, 2, 0.0),          # element path
     ("fp32", 1024, 8, 0.2),
     ("fp32", 4, 1, 0.0),            # one 16-byte unit per row
+    ("bf16", 4099, 2, 0.05),        # element path, rows shared by five workgroups (column blocks)
 ]
 
 
