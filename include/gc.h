@@ -20,6 +20,8 @@
  *     means nothing was enqueued.  GC_ERR_HIP means a launch failed; faults
  *     inside a kernel surface at the caller's next synchronisation.
  *   - No call allocates device memory.  The bucket plan is a host object.
+ *   - No call memsets, copies through the host or synchronises, so calls can
+ *     be captured into a HIP graph and replayed (validation runs at capture).
  *   - nranks is 1..GC_MAX_RANKS.  Element counts are per rank.
  *   - Calls are reentrant; concurrent calls on different streams must not
  *     write overlapping memory.
