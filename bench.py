@@ -728,10 +728,10 @@ def cpu_baseline(w, seed):
     run()  # warm the code paths once (numpy allocations)
     t0 = time.perf_counter()
     reps = 0
-    while True:
+    while True:  # about 10 s of single-threaded oracle work
         run()
         reps += 1
-        if time.perf_counter() - t0 >= 10.0 or reps >= 20:
+        if time.perf_counter() - t0 >= 10.0 or reps >= 1000:
             break
     per = (time.perf_counter() - t0) / reps
     model, threads = host_cpu()
