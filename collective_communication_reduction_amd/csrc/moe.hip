@@ -238,6 +238,12 @@ __global__ void __launch_bounds__(kThreads) route_final_kernel(const RouteArgs<P
 // rows or buffers are not 16-byte aligned).  S = 2^lanes_log2 lanes work on a
 // row, kMoeU units per lane per step (all loads of a step issued before the
 // first store); a workgroup holds kThreads / S rows.
+//
+// Dispatch with WROW (S >= 64): every wavefront lies inside one row, so a
+// route's (rank, row) entry is the same on all of its lanes.  It is moved to
+// scalar registers, and the destination's base pointer and row count then
+// come from the kernel arguments by scalar loads: one vector round trip per
+// batch of routes instead of three dependent ones per route.
 
 #ifndef GC_MOE_UNITS
 #define GC_MOE_UNITS 4
@@ -268,17 +274,33 @@ __device__ __forceinline__ void st_unit(T* p, T v) {
   else __builtin_nontemporal_store(v, p);
 }
 
-// Rank and row of route (t, k) as a unit pointer into its destination, or
-// nullptr when the entry lies outside the destination buffers.
-template <class T, int P>
+// A route's (rank, row) entry as a unit pointer into its destination, or
+// nullptr when the entry lies outside the destination buffers.  Branch-free:
+// the rank index is clamped so that the base pointer and row count are always
+// loaded (in bounds) and the loads of several routes issue together.  With
+// WROW the entry is first made wavefront-uniform, so both are scalar loads.
+template <class T, bool WROW, int P>
 __device__ __forceinline__ T* route_row(char* const (&buf)[P], const int64_t (&rows)[P], int N, int2 p,
                                         uint64_t R) {
-  if (p.x < 0 || p.x >= N || p.y < 0 || p.y >= rows[p.x]) return nullptr;
-  return reinterpret_cast<T*>(buf[p.x]) + static_cast<uint64_t>(p.y) * R;
+  if constexpr (WROW) p = make_int2(__builtin_amdgcn_readfirstlane(p.x), __builtin_amdgcn_readfirstlane(p.y));
+  const int q = min(max(p.x, 0), N - 1);
+  const int64_t nrows = rows[q];
+  char* const base = buf[q];
+  const bool ok = p.x >= 0 && p.x < N && p.y >= 0 && p.y < nrows;
+  return ok ? reinterpret_cast<T*>(base) + static_cast<uint64_t>(p.y) * R : nullptr;
 }
 
-template <class T, int P>
+// Routes resolved per batch: all K at once when K is known at compile time, else four.
+template <int KT>
+constexpr int route_batch() { return KT > 0 ? KT : 4; }
+
+// KT > 0: K == KT known at compile time.  The K destinations of a step are
+// resolved together, after its loads are issued and before any store, so no
+// route waits on the previous route's stores.
+template <class T, int KT, bool WROW, int P>
 __global__ void __launch_bounds__(kThreads) dispatch_kernel(const DispatchArgs<P> a) {
+  constexpr int KB = route_batch<KT>();
+  const int K = KT > 0 ? KT : a.K;
   const int S = 1 << a.lanes_log2;
   const int sub = threadIdx.x >> a.lanes_log2, lane = threadIdx.x & (S - 1);
   const int G = kThreads >> a.lanes_log2;
@@ -292,7 +314,7 @@ __global__ void __launch_bounds__(kThreads) dispatch_kernel(const DispatchArgs<P
     const uint64_t cbeg = static_cast<uint64_t>(local % a.cb) * span;
     const uint64_t cend = a.cb > 1 ? min(a.R, cbeg + span) : a.R;
     const T* src = reinterpret_cast<const T*>(a.tok[s]) + static_cast<uint64_t>(t) * a.R;
-    const int2* dst = a.dest[s] + t * a.K;
+    const int2* dst = a.dest[s] + t * K;
     for (uint64_t c = cbeg + lane; c < cend; c += span) {
       T v[kMoeU];
 #pragma unroll
@@ -300,13 +322,21 @@ __global__ void __launch_bounds__(kThreads) dispatch_kernel(const DispatchArgs<P
         const uint64_t cj = c + static_cast<uint64_t>(j) * S;
         v[j] = ld_unit(src + (cj < cend ? cj : c));  // clamped: no exec-masked load
       }
-      for (int k = 0; k < a.K; ++k) {
-        T* out = route_row<T, P>(a.recv, a.recv_rows, a.N, dst[k], a.R);
-        if (!out) continue;
+      for (int k0 = 0; k0 < K; k0 += KB) {
+        int2 e[KB];
 #pragma unroll
-        for (int j = 0; j < kMoeU; ++j) {
-          const uint64_t cj = c + static_cast<uint64_t>(j) * S;
-          if (j == 0 || cj < cend) st_unit(out + cj, v[j]);
+        for (int i = 0; i < KB; ++i) e[i] = KT > 0 || k0 + i < K ? dst[k0 + i] : make_int2(-1, -1);
+        T* out[KB];
+#pragma unroll
+        for (int i = 0; i < KB; ++i) out[i] = route_row<T, WROW, P>(a.recv, a.recv_rows, a.N, e[i], a.R);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+          if (!out[i]) continue;
+#pragma unroll
+          for (int j = 0; j < kMoeU; ++j) {
+            const uint64_t cj = c + static_cast<uint64_t>(j) * S;
+            if (j == 0 || cj < cend) st_unit(out[i] + cj, v[j]);
+          }
         }
       }
     }
@@ -372,6 +402,10 @@ __device__ __forceinline__ void accumulate(float (&acc)[VE], const float (&y)[VE
 }
 
 // KT > 0: K == KT known at compile time (all K loads of a step in flight at once).
+// Routes are looked up per lane even when a wavefront lies in one row: the
+// combine's row reads scatter over every expert block, and on MI355X issuing
+// them sooner through the scalar lookup made it slower (529 vs 506 us for 8 x
+// 16384 tokens x 8 KiB rows, top-2), unlike the dispatch.
 template <class In, bool VEC, int KT, int P>
 __global__ void __launch_bounds__(kThreads) combine_kernel(const CombineArgs<P> a) {
   typedef Unit<In, VEC> U;
@@ -409,7 +443,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const CombineArgs<P> 
         float wk[KB];
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
-          const T* row = route_row<T, P>(a.y, a.y_rows, a.N, routes[k0 + j], a.R);
+          const T* row = route_row<T, false, P>(a.y, a.y_rows, a.N, routes[k0 + j], a.R);
           ok[j] = row != nullptr;
           wk[j] = wt[k0 + j];
           if (ok[j]) {
@@ -525,6 +559,15 @@ gc_status route_impl(const gci::MoeRouteCall& c) {
   return launch(route_final_kernel<P>, a, tiles, kThreads, lds, c.stream);
 }
 
+template <class T, bool WROW, int P>
+gc_status launch_dispatch(const DispatchArgs<P>& a, int topk, uint32_t grid, hipStream_t stream) {
+  switch (topk) {
+    case 1: return launch(dispatch_kernel<T, 1, WROW, P>, a, grid, kThreads, 0, stream);
+    case 2: return launch(dispatch_kernel<T, 2, WROW, P>, a, grid, kThreads, 0, stream);
+    default: return launch(dispatch_kernel<T, 0, WROW, P>, a, grid, kThreads, 0, stream);
+  }
+}
+
 template <class T, int P>
 gc_status dispatch_impl(const gci::MoeMoveCall& c, uint64_t R) {
   DispatchArgs<P> a{};
@@ -542,7 +585,17 @@ gc_status dispatch_impl(const gci::MoeMoveCall& c, uint64_t R) {
   fill_groups<P>(a.grp0, a.ntok, c.tokens, c.nranks, kThreads >> a.lanes_log2, a.cb);
   if (a.grp0[c.nranks] == 0) return GC_OK;
   const uint32_t grid = std::min<uint32_t>(a.grp0[c.nranks], GC_MOE_MAX_GRID);
-  return launch(dispatch_kernel<T, P>, a, grid, kThreads, 0, c.stream);
+  if (a.lanes_log2 >= 6) return launch_dispatch<T, true, P>(a, c.topk, grid, c.stream);
+  return launch_dispatch<T, false, P>(a, c.topk, grid, c.stream);
+}
+
+template <class In, bool VEC, int P>
+gc_status launch_combine(const CombineArgs<P>& a, int topk, uint32_t grid, hipStream_t stream) {
+  switch (topk) {
+    case 1: return launch(combine_kernel<In, VEC, 1, P>, a, grid, kThreads, 0, stream);
+    case 2: return launch(combine_kernel<In, VEC, 2, P>, a, grid, kThreads, 0, stream);
+    default: return launch(combine_kernel<In, VEC, 0, P>, a, grid, kThreads, 0, stream);
+  }
 }
 
 template <class In, bool VEC, int P>
@@ -563,11 +616,7 @@ gc_status combine_impl(const gci::MoeMoveCall& c, uint64_t R) {
   fill_groups<P>(a.grp0, a.ntok, c.tokens, c.nranks, kThreads >> a.lanes_log2, a.cb);
   if (a.grp0[c.nranks] == 0) return GC_OK;
   const uint32_t grid = std::min<uint32_t>(a.grp0[c.nranks], GC_MOE_MAX_GRID);
-  switch (c.topk) {
-    case 1: return launch(combine_kernel<In, VEC, 1, P>, a, grid, kThreads, 0, c.stream);
-    case 2: return launch(combine_kernel<In, VEC, 2, P>, a, grid, kThreads, 0, c.stream);
-    default: return launch(combine_kernel<In, VEC, 0, P>, a, grid, kThreads, 0, c.stream);
-  }
+  return launch_combine<In, VEC, P>(a, c.topk, grid, c.stream);
 }
 
 template <int P>

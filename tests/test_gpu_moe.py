@@ -128,6 +128,33 @@ def test_dispatch(row_bytes, offset):
         assert np.all(got[n:] == 0xA5), f"rank {d} wrote past its rows"
 
 
+@pytest.mark.parametrize("K", [1, 3, 5])
+@pytest.mark.parametrize("row_bytes", [8192, 4100, 48])
+def test_dispatch_topk(K, row_bytes):
+    """Routes per token with and without a compiled-in count (1 and 2 are; 3 and 5
+    go through batches of four), on rows a wavefront shares (8192: 16-byte
+    units; 4100: 4-byte units) and on rows several share a wavefront (48)."""
+    rng = np.random.default_rng(1000 * K + row_bytes)
+    N, E = 3, 4
+    T = [41, 7, 0]
+    experts = _routing(rng, N, E, T, K, drop=0.1)
+    ntok, splits, dest = route_on_device(experts, N, E, K)
+    want_splits = check_plan(experts, N, E, K, splits, dest)
+    tokens = [_byte_rows(rng, t, row_bytes) for t in T]
+    want = M.dispatch(tokens, experts, N, E, row_bytes)
+    rows = want_splits.sum(axis=(0, 2))
+    tok_dev = [torch.from_numpy(t).to(DEV) if t.size else torch.zeros(16, dtype=torch.uint8, device=DEV)
+               for t in tokens]
+    recv = [torch.full((max(16, (int(r) + 2) * row_bytes),), 0x5A, dtype=torch.uint8, device=DEV) for r in rows]
+    gc.gc_moe_dispatch(tok_dev, ntok, dest, K, row_bytes, recv, [int(r) + 2 for r in rows])
+    torch.cuda.synchronize()
+    for d in range(N):
+        got = from_dev(recv[d])
+        n = int(rows[d]) * row_bytes
+        assert np.array_equal(got[:n], want[d]), f"rank {d}"
+        assert np.all(got[n:] == 0x5A), f"rank {d} wrote past its rows"
+
+
 def _expert_rows(rng, n, hidden, dtype, special):
     x = rng.normal(size=n * hidden).astype(np.float32)
     if special and x.size >= 8:
@@ -197,9 +224,12 @@ def test_dispatch_then_combine_round_trip(dtype):
         assert_same(from_dev(out[s]), want[s], dtype, f"source {s}")
 
 
-def test_malformed_plan_entries_are_skipped():
-    """Entries naming a rank or row outside the buffers are skipped, not followed."""
-    N, K, H = 2, 2, 8
+@pytest.mark.parametrize("H", [8, 1024])
+def test_malformed_plan_entries_are_skipped(H):
+    """Entries naming a rank or row outside the buffers are skipped, not followed.
+    H = 1024 fp32 (4 KiB rows) puts whole wavefronts on one row, where the
+    dispatch reads each entry once per wavefront."""
+    N, K = 2, 2
     dest = [_i32([[0, 0], [5, 0], [1, 1], [1, 99], [-1, 0], [0, -3]]), _i32([[1, 0], [0, 1]])]
     ntok = [3, 1]
     tokens = [torch.arange(3 * H, dtype=torch.float32, device=DEV) + 1, torch.full((H,), -1.0, device=DEV)]
