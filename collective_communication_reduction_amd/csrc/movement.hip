@@ -11,6 +11,7 @@
 // workgroup the same number of bytes.
 
 #include <algorithm>
+#include <cstdint>
 
 #include "device_common.h"
 #include "gc_internal.h"
@@ -22,39 +23,92 @@ using namespace gcdev;
 // ------------------------------------------------------------ segment copy
 
 constexpr int kMaxSeg = 128;  // kernel arguments: 3.6 KiB of the 4 KiB limit
+constexpr int kSegGroup = 16;                     // segments per lookup group
+constexpr int kSegGroups = kMaxSeg / kSegGroup;
 #ifndef GC_SEG_U
 #define GC_SEG_U 1
 #endif
 constexpr int kSegU = GC_SEG_U;                   // 16-byte vectors per thread per tile
 constexpr uint64_t kSegTileVec = kThreads * kSegU;
 
-struct SegArgs {
-  const char* src[kMaxSeg];  // nullptr: fill with zeros
-  char* dst[kMaxSeg];
-  uint64_t bytes[kMaxSeg];
-  uint32_t tile0[kMaxSeg + 1];  // first tile of each segment; tile0[nseg] = total
-  uint32_t nseg;
+struct SegDesc {
+  const char* src;  // nullptr: fill with zeros
+  char* dst;
+  uint64_t bytes;
 };
 
-__device__ __forceinline__ uint32_t find_segment(const SegArgs& a, uint32_t tile) {
-  uint32_t lo = 0, hi = a.nseg;  // last s with tile0[s] <= tile
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) / 2;
-    if (a.tile0[mid] <= tile) lo = mid; else hi = mid;
+struct SegArgs {
+  SegDesc seg[kMaxSeg];
+  uint32_t tile0[kMaxSeg];         // first tile of each segment; UINT32_MAX past the last
+  uint32_t coarse[kSegGroups];     // tile0[kSegGroup * g]; UINT32_MAX for unused groups
+  uint32_t nseg, ntiles;
+};
+static_assert(sizeof(SegArgs) <= 4096, "segment table must fit the kernel argument limit");
+
+// Launch-wide lookup state, read once per workgroup before its first tile:
+// with these the segment of a tile takes at most two dependent scalar loads
+// (the tile starts of its group of 16 segments, then its descriptor), and a
+// one-segment launch none.  A workgroup copies only 4 KiB, so its life is
+// about one HBM round trip; a binary search over the tile table (seven
+// dependent loads at 128 segments) kept fewer bytes in flight.
+struct SegLookup {
+  uint32_t ntiles, nseg;
+  uint32_t coarse[kSegGroups];
+  SegDesc first;
+};
+
+__device__ __forceinline__ SegLookup seg_lookup(const SegArgs& a) {
+  SegLookup l;
+  l.ntiles = a.ntiles;
+  l.nseg = a.nseg;
+#pragma unroll
+  for (int i = 0; i < kSegGroups; ++i) l.coarse[i] = a.coarse[i];
+  l.first = a.seg[0];
+  return l;
+}
+
+// Segment of `tile` and the tile's index inside it.
+__device__ __forceinline__ SegDesc find_segment(const SegArgs& a, const SegLookup& l, uint32_t tile, uint32_t& t) {
+  if (l.nseg == 1) {
+    t = tile;
+    return l.first;
   }
-  return lo;
+  // Group g: the last whose first tile is <= tile (selects only: a dynamic
+  // index into a local array would put it, and the argument block, in scratch).
+  uint32_t g = 0, start = l.coarse[0];
+#pragma unroll
+  for (int i = 1; i < kSegGroups; ++i) {
+    if (l.coarse[i] <= tile) {
+      g = i;
+      start = l.coarse[i];
+    }
+  }
+  uint32_t j = 0;
+#pragma unroll
+  for (int i = 1; i < kSegGroup; ++i) {
+    const uint32_t v = a.tile0[g * kSegGroup + i];  // ascending; UINT32_MAX past the last segment
+    if (v <= tile) {
+      j = i;
+      start = v;
+    }
+  }
+  t = tile - start;
+  return a.seg[g * kSegGroup + j];
 }
 
 // Segments whose source and destination agree modulo 16 bytes: byte head up
 // to the first 16-byte boundary of the destination, 16-byte body, byte tail.
 __global__ void __launch_bounds__(kThreads) segment_vec_kernel(const SegArgs a) {
-  const uint32_t ntiles = a.tile0[a.nseg];
-  for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const uint32_t s = find_segment(a, tile);
-    const uint32_t t = tile - a.tile0[s];
-    const char* src = a.src[s];
-    char* dst = a.dst[s];
-    const uint64_t n = a.bytes[s];
+  const SegLookup l = seg_lookup(a);
+  // The grid never exceeds the tile count, so every workgroup has a first tile
+  // (no guard ahead of it: all lookup loads issue together).
+  uint32_t tile = blockIdx.x;
+  do {
+    uint32_t t;
+    const SegDesc d = find_segment(a, l, tile, t);
+    const char* src = d.src;
+    char* dst = d.dst;
+    const uint64_t n = d.bytes;
     const uint64_t head = min<uint64_t>(n, (16 - (reinterpret_cast<uint64_t>(dst) & 15)) & 15);
     const uint64_t nvec = (n - head) / 16;
     const uint64_t tail_beg = head + nvec * 16;
@@ -80,34 +134,38 @@ __global__ void __launch_bounds__(kThreads) segment_vec_kernel(const SegArgs a) 
         dst[b] = src ? src[b] : 0;
       }
     }
-  }
+    tile += gridDim.x;
+  } while (tile < l.ntiles);
 }
 
 // Segments with mismatched alignment: W-byte elements (W divides both
 // addresses and the length).
 template <typename T>
 __global__ void __launch_bounds__(kThreads) segment_narrow_kernel(const SegArgs a) {
-  const uint32_t ntiles = a.tile0[a.nseg];
+  const SegLookup l = seg_lookup(a);
   constexpr uint64_t TE = kThreads * 8;
-  for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const uint32_t s = find_segment(a, tile);
-    const uint32_t t = tile - a.tile0[s];
-    const T* src = reinterpret_cast<const T*>(a.src[s]);
-    T* dst = reinterpret_cast<T*>(a.dst[s]);
-    const uint64_t n = a.bytes[s] / sizeof(T);
-    if (static_cast<uint64_t>(t) * TE >= n) continue;
-    T buf[8];
+  uint32_t tile = blockIdx.x;  // the grid never exceeds the tile count
+  do {
+    uint32_t t;
+    const SegDesc d = find_segment(a, l, tile, t);
+    const T* src = reinterpret_cast<const T*>(d.src);
+    T* dst = reinterpret_cast<T*>(d.dst);
+    const uint64_t n = d.bytes / sizeof(T);
+    if (static_cast<uint64_t>(t) * TE < n) {
+      T buf[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint64_t e = min(static_cast<uint64_t>(t) * TE + u * kThreads + threadIdx.x, n - 1);
-      buf[u] = src ? src[e] : T(0);
-    }
+      for (int u = 0; u < 8; ++u) {
+        const uint64_t e = min(static_cast<uint64_t>(t) * TE + u * kThreads + threadIdx.x, n - 1);
+        buf[u] = src ? src[e] : T(0);
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint64_t e = static_cast<uint64_t>(t) * TE + u * kThreads + threadIdx.x;
-      if (e < n) dst[e] = buf[u];
+      for (int u = 0; u < 8; ++u) {
+        const uint64_t e = static_cast<uint64_t>(t) * TE + u * kThreads + threadIdx.x;
+        if (e < n) dst[e] = buf[u];
+      }
     }
-  }
+    tile += gridDim.x;
+  } while (tile < l.ntiles);
 }
 
 // ------------------------------------------------------------ host side
@@ -141,12 +199,13 @@ bool vec_ok(const gci::Segment& s) { return !s.src || ((addr(s.src) ^ addr(s.dst
 // Launch one batch of segments of one class (width 16 = vector kernel).
 gc_status launch_batch(const gci::Segment* segs, int n, int width, hipStream_t stream) {
   SegArgs a{};
+  std::fill(a.tile0, a.tile0 + kMaxSeg, UINT32_MAX);
+  std::fill(a.coarse, a.coarse + kSegGroups, UINT32_MAX);
   uint32_t tiles = 0;
   for (int i = 0; i < n; ++i) {
-    a.src[i] = static_cast<const char*>(segs[i].src);
-    a.dst[i] = static_cast<char*>(segs[i].dst);
-    a.bytes[i] = segs[i].bytes;
+    a.seg[i] = SegDesc{static_cast<const char*>(segs[i].src), static_cast<char*>(segs[i].dst), segs[i].bytes};
     a.tile0[i] = tiles;
+    if (i % kSegGroup == 0) a.coarse[i / kSegGroup] = tiles;
     uint64_t units;
     if (width == 16) {
       const uint64_t head = std::min<uint64_t>(segs[i].bytes, (16 - (addr(segs[i].dst) & 15)) & 15);
@@ -157,7 +216,7 @@ gc_status launch_batch(const gci::Segment* segs, int n, int width, hipStream_t s
       tiles += static_cast<uint32_t>(std::max<uint64_t>(1, (units + kThreads * 8 - 1) / (kThreads * 8)));
     }
   }
-  a.tile0[n] = tiles;
+  a.ntiles = tiles;
   a.nseg = static_cast<uint32_t>(n);
   const uint32_t grid = std::min(tiles, kMaxGrid);
   switch (width) {
