@@ -274,6 +274,29 @@ def test_all_to_all(N, E, row_bytes):
         assert np.array_equal(got, want[d]), f"rank {d}"
 
 
+@pytest.mark.parametrize("misalign", [0, 4])
+@pytest.mark.parametrize("nblocks", [1, 2, 15, 16, 17, 31, 33, 127, 128, 129, 300])
+def test_all_to_all_segment_counts(nblocks, misalign):
+    """One rank, `nblocks` experts with rows in every block: each block is one
+    segment of the copy (at most 128 per launch, looked up in groups of 16),
+    with blocks from one row to several 4 KiB tiles.  misalign = 4 shifts the
+    receive buffer so that every segment takes the narrow-width copy."""
+    rng = np.random.default_rng(nblocks * 10 + misalign)
+    rb = 16
+    splits = rng.integers(1, 700, size=(1, 1, nblocks)).astype(np.int64)
+    splits[0, 0, rng.integers(0, nblocks, size=max(1, nblocks // 8))] = 1
+    sends = [rng.integers(0, 256, size=int(splits.sum()) * rb, dtype=np.uint8)]
+    want = C.all_to_all(sends, splits, rb)
+    send = [torch.from_numpy(sends[0]).to(DEV)]
+    recv_full = torch.full((misalign + len(want[0]) + 64,), 0xC3, dtype=torch.uint8, device=DEV)
+    recv = [recv_full[misalign:misalign + len(want[0])]]
+    gc.gc_all_to_all(send, recv, splits, rb)
+    torch.cuda.synchronize()
+    got = recv_full.cpu().numpy()
+    assert np.array_equal(got[misalign:misalign + len(want[0])], want[0])
+    assert np.all(got[:misalign] == 0xC3) and np.all(got[misalign + len(want[0]):] == 0xC3)
+
+
 def test_all_to_all_skewed_single_destination():
     # every row to rank 0, expert 0: one hot destination
     N, E, rb = 8, 8, 256
