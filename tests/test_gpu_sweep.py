@@ -1,0 +1,163 @@
+"""Seeded random sweep of the reduction calls against the oracle: rank counts
+(odd, prime, up to 64), lengths from empty to a few hundred thousand elements
+(log-uniform, so ragged tails and short chunks are common), element types,
+ops, fold orders, both all-reduce algorithms, buffer views starting a few
+elements into their allocation (a common phase keeps the vector kernels and
+moves every chunk edge; differing phases take the element kernels), and in
+place.  Each case is drawn from its own seed, printed in the test id, so a
+failure names a case that reruns alone.
+
+Tolerance as in the parity tests: bit-exact for fp32, int32 and movement;
+bf16 within 1 ulp and expected bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import collective_communication_reduction_amd as gc
+from gen import host as G
+from oracle import collectives as C
+from oracle import hierarchical as H
+from tests.gpu_util import DEV, assert_same, empty, from_dev, max_ulp, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RANKS = [1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 31, 33, 63, 64]
+REDUCE_TYPES = [("bf16", "bf16", "avg"), ("bf16", "bf16", "sum"), ("fp32", "fp32", "sum"), ("fp32", "fp32", "avg"),
+                ("int32", "int32", "sum")]
+RS_TYPES = REDUCE_TYPES + [("bf16", "fp32", "avg"), ("fp32", "bf16", "avg")]
+
+
+def _values(dtype, N, S, seed):
+    out = []
+    for r in range(N):
+        key, idx = G.stream_key(seed, r, 0), np.arange(S)
+        if dtype == "bf16":
+            out.append(G.normal_bf16(key, idx, 1e-3))
+        elif dtype == "fp32":
+            out.append(G.uniform_f32(key, idx))
+        else:
+            out.append(G.int32_values(key, idx))
+    return out
+
+
+def _length(rng, hi):
+    return int(np.exp(rng.uniform(0.0, np.log(hi + 1.0)))) - 1
+
+
+def _offsets(rng, N):
+    """Element offsets of the N views: one common offset, or one per rank."""
+    if rng.random() < 0.5:
+        return [int(rng.integers(0, 8))] * N
+    return [int(x) for x in rng.integers(0, 8, size=N)]
+
+
+def _views(n, dtype, offsets):
+    return [empty(n + 8, dtype)[o:o + n] for o in offsets]
+
+
+def _check(got, want, dtype, what):
+    if dtype == "bf16":
+        assert max_ulp(got, want) <= 1, what
+    assert_same(got, want, dtype, what)
+
+
+def _sample_ranks(N):
+    return sorted({0, N // 2, N - 1})
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_all_reduce_sweep(seed):
+    rng = np.random.default_rng(7000 + seed)
+    N = int(rng.choice(RANKS))
+    S = _length(rng, 250_000)
+    dtype, _, op = REDUCE_TYPES[int(rng.integers(len(REDUCE_TYPES)))]
+    order = str(rng.choice(["ring", "rank", "ring_wire"]))
+    algo = str(rng.choice(["fused", "rs_ag"]))
+    in_place = algo == "fused" and rng.random() < 0.25
+    offs_in = _offsets(rng, N)
+    offs_out = offs_in if in_place else _offsets(rng, N)
+    case = f"N={N} S={S} {dtype} {op} {order} {algo} in_place={in_place} in={offs_in[:4]} out={offs_out[:4]}"
+    xs = _values(dtype, N, S, seed)
+    want = C.all_reduce(xs, dtype, op, order)[0] if S else np.zeros(0)
+    send = _views(S, dtype, offs_in)
+    for v, x in zip(send, xs):
+        v.copy_(to_dev(x, dtype))
+    recv = send if in_place else _views(S, dtype, offs_out)
+    scratch = torch.empty(max(1, gc.gc_all_reduce_scratch_bytes(S, N, dtype)), dtype=torch.uint8, device=DEV)
+    gc.gc_all_reduce(send, recv, op=op, order=order, algo=algo, scratch=scratch)
+    torch.cuda.synchronize()
+    for r in _sample_ranks(N):
+        _check(from_dev(recv[r]), want, dtype, f"{case} rank {r}")
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_reduce_scatter_sweep(seed):
+    rng = np.random.default_rng(8000 + seed)
+    N = int(rng.choice(RANKS))
+    rc = _length(rng, 20_000)
+    tin, tout, op = RS_TYPES[int(rng.integers(len(RS_TYPES)))]
+    order = str(rng.choice(["ring", "rank", "ring_wire"]))
+    in_place = tin == tout and rng.random() < 0.3
+    offs_in = _offsets(rng, N)
+    case = f"N={N} rc={rc} {tin}->{tout} {op} {order} in_place={in_place} in={offs_in[:4]}"
+    xs = _values(tin, N, N * rc, seed)
+    want = C.reduce_scatter(xs, tin, tout, op, order) if rc else [np.zeros(0)] * N
+    send = _views(N * rc, tin, offs_in)
+    for v, x in zip(send, xs):
+        v.copy_(to_dev(x, tin))
+    if in_place:
+        recv = [send[r][r * rc:(r + 1) * rc] for r in range(N)]
+    else:
+        recv = _views(rc, tout, _offsets(rng, N))
+    gc.gc_reduce_scatter(send, recv, op=op, order=order)
+    torch.cuda.synchronize()
+    for j in _sample_ranks(N):
+        _check(from_dev(recv[j]), want[j], tout, f"{case} owner {j}")
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_all_gather_sweep(seed):
+    rng = np.random.default_rng(9000 + seed)
+    N = int(rng.choice(RANKS))
+    count = _length(rng, 30_000)
+    dtype = str(rng.choice(["bf16", "fp32", "int32"]))
+    in_place = rng.random() < 0.3
+    offs_out = _offsets(rng, N)
+    case = f"N={N} count={count} {dtype} in_place={in_place} out={offs_out[:4]}"
+    shards = _values(dtype, N, count, seed)
+    want = C.all_gather(shards) if count else [np.zeros(0)] * N
+    recv = _views(N * count, dtype, offs_out)
+    if in_place:
+        send = [recv[r][r * count:(r + 1) * count] for r in range(N)]
+    else:
+        send = _views(count, dtype, _offsets(rng, N))
+    for v, x in zip(send, shards):
+        v.copy_(to_dev(x, dtype))
+    gc.gc_all_gather(send, recv)
+    torch.cuda.synchronize()
+    for d in _sample_ranks(N):
+        assert_same(from_dev(recv[d]), want[d], dtype, f"{case} rank {d}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_two_level_all_reduce_sweep(seed):
+    rng = np.random.default_rng(10000 + seed)
+    N = int(rng.choice([2, 4, 6, 8, 9, 12, 16, 32, 64]))
+    groups = [g for g in range(1, N + 1) if N % g == 0]
+    Sg = int(rng.choice(groups))
+    S = _length(rng, 200_000)
+    dtype, _, op = REDUCE_TYPES[int(rng.integers(len(REDUCE_TYPES)))]
+    order = str(rng.choice(["ring", "rank"]))
+    offs = _offsets(rng, N)
+    case = f"N={N} group={Sg} S={S} {dtype} {op} {order} offsets={offs[:4]}"
+    xs = _values(dtype, N, S, seed)
+    want = H.all_reduce(xs, Sg, dtype, op, order)[0] if S else np.zeros(0)
+    send = _views(S, dtype, offs)
+    for v, x in zip(send, xs):
+        v.copy_(to_dev(x, dtype))
+    recv = _views(S, dtype, _offsets(rng, N))
+    gc.gc_hier_all_reduce(send, recv, Sg, op=op, order=order)
+    torch.cuda.synchronize()
+    for r in _sample_ranks(N):
+        _check(from_dev(recv[r]), want, dtype, f"{case} rank {r}")
