@@ -161,3 +161,71 @@ def test_two_level_all_reduce_sweep(seed):
     torch.cuda.synchronize()
     for r in _sample_ranks(N):
         _check(from_dev(recv[r]), want, dtype, f"{case} rank {r}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_hsdp_reduce_scatter_sweep(seed):
+    rng = np.random.default_rng(11000 + seed)
+    N = int(rng.choice([2, 4, 6, 8, 9, 12, 16, 32, 64]))
+    Sg = int(rng.choice([g for g in range(1, N + 1) if N % g == 0]))
+    rc = _length(rng, 20_000)
+    tin, tout, op = RS_TYPES[int(rng.integers(len(RS_TYPES)))]
+    order = str(rng.choice(["ring", "rank"]))
+    in_place = tin == tout and rng.random() < 0.3
+    offs = _offsets(rng, N)
+    case = f"N={N} group={Sg} rc={rc} {tin}->{tout} {op} {order} in_place={in_place} offsets={offs[:4]}"
+    xs = _values(tin, N, Sg * rc, seed)
+    want = H.hsdp_reduce_scatter(xs, Sg, tin, tout, op, order) if rc else [np.zeros(0)] * N
+    send = _views(Sg * rc, tin, offs)
+    for v, x in zip(send, xs):
+        v.copy_(to_dev(x, tin))
+    if in_place:
+        recv = [send[r][(r % Sg) * rc:(r % Sg + 1) * rc] for r in range(N)]
+    else:
+        recv = _views(rc, tout, _offsets(rng, N))
+    gc.gc_hsdp_reduce_scatter(send, recv, Sg, op=op, order=order)
+    torch.cuda.synchronize()
+    for r in _sample_ranks(N):
+        _check(from_dev(recv[r]), want[r], tout, f"{case} rank {r}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_fsdp2_sweep(seed):
+    """Random parameter lists (including rows < N, so trailing ranks hold empty
+    shards, and empty parameters): per-parameter dim-0 reduce-scatter, then the
+    all-gather of the oracle's shards."""
+    from oracle import fsdp2 as F2
+    rng = np.random.default_rng(12000 + seed)
+    N = int(rng.choice(RANKS))
+    P = int(rng.integers(1, 10))
+    budget = 2_000_000 // max(N, 1)                  # elements per rank over all parameters
+    rows = [int(x) for x in rng.integers(0, 3 * N + 2, size=P)]
+    for p in rng.choice(P, size=min(P, 2), replace=False):
+        rows[p] = int(rng.integers(1, 5000))
+    cols = [int(rng.integers(0, 300)) for _ in range(P)]
+    while sum(r * c for r, c in zip(rows, cols)) > budget:
+        p = int(np.argmax([r * c for r, c in zip(rows, cols)]))
+        rows[p] //= 2
+    tin, tout, op = RS_TYPES[int(rng.integers(len(RS_TYPES)))]
+    order = str(rng.choice(["ring", "rank", "ring_wire"]))
+    case = f"N={N} rows={rows} cols={cols} {tin}->{tout} {op} {order}"
+    grads = [[_values(tin, 1, rows[p] * cols[p], seed * 100 + r * 10 + p)[0] for p in range(P)] for r in range(N)]
+    want = F2.reduce_scatter(grads, rows, cols, tin, tout, op, order)
+    g_dev = [[to_dev(grads[r][p], tin) for p in range(P)] for r in range(N)]
+    lens = [[hi - lo for lo, hi in F2.shard_elems(rows[p], cols[p], N)] for p in range(P)]
+    shards = [[empty(lens[p][r], tout) if lens[p][r] else 0 for p in range(P)] for r in range(N)]
+    gc.gc_fsdp2_reduce_scatter(g_dev, shards, rows, cols, N, tin, tout, op, order)
+    torch.cuda.synchronize()
+    for r in _sample_ranks(N):
+        for p in range(P):
+            if lens[p][r]:
+                _check(from_dev(shards[r][p]), want[r][p], tout, f"{case} rank {r} param {p}")
+    # all-gather the oracle's shards back into full parameters
+    s_dev = [[to_dev(want[r][p], tout) if lens[p][r] else 0 for p in range(P)] for r in range(N)]
+    full = [[empty(rows[p] * cols[p], tout) for p in range(P)] for _ in range(N)]
+    gc.gc_fsdp2_all_gather(s_dev, full, rows, cols, N, tout)
+    torch.cuda.synchronize()
+    want_full = F2.all_gather(want, rows, cols, tout)
+    for d in _sample_ranks(N):
+        for p in range(P):
+            assert_same(from_dev(full[d][p]), want_full[d][p], tout, f"{case} all-gather rank {d} param {p}")
