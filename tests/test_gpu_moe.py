@@ -129,11 +129,12 @@ def test_dispatch(row_bytes, offset):
 
 
 @pytest.mark.parametrize("K", [1, 3, 5])
-@pytest.mark.parametrize("row_bytes", [8192, 4100, 48])
+@pytest.mark.parametrize("row_bytes", [8192, 4100, 1001, 48])
 def test_dispatch_topk(K, row_bytes):
     """Routes per token with and without a compiled-in count (1 and 2 are; 3 and 5
     go through batches of four), on rows a wavefront shares (8192: 16-byte
-    units; 4100: 4-byte units) and on rows several share a wavefront (48)."""
+    units; 4100: 4-byte units; 1001: 1-byte units) and on rows several share a
+    wavefront (48)."""
     rng = np.random.default_rng(1000 * K + row_bytes)
     N, E = 3, 4
     T = [41, 7, 0]
