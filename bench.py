@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--layout", default="arena", choices=["arena", "staggered", "separate"],
                    help="placement of the rank buffers in HBM")
     p.add_argument("--stagger", type=int, default=4096, help="extra bytes between consecutive ranks' memory")
+    p.add_argument("--max-region", type=int, default=32, metavar="GIB",
+                   help="largest per-rank region of the rank arena (a power of two, GiB)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-copy-ceiling", action="store_true", help="skip the 2 GiB copy-ceiling measurement")
@@ -127,7 +129,8 @@ class Layout:
         self.kind = args.layout
         self.nranks = nranks
         self.stagger = args.stagger
-        self.arena = gc.RankArena(nranks, stagger_bytes=args.stagger) if self.kind == "arena" else None
+        self.arena = (gc.RankArena(nranks, stagger_bytes=args.stagger, max_region=args.max_region << 30)
+                      if self.kind == "arena" else None)
 
     def buffers(self, count, tdt):
         import torch

@@ -436,7 +436,7 @@ def test_wire_bf16_ring_error_study():
               f"median {stats[order][1]:.3e}, p99 {stats[order][2]:.3e}, max {stats[order][3]:.3e} "
               f"({len(pos)} samples)", flush=True)
     assert stats["ring_wire"][1] > stats["ring"][1] and stats["ring_wire"][0] > stats["ring"][0]
-    del send, recv
+    del send, recv, arena                                     # release the 8-rank arena before the 64-rank one
     torch.cuda.empty_cache()
 
     N = WORKLOADS["fsdp_layer_n64"]["nranks"]
@@ -503,7 +503,7 @@ def test_hier_ar_n16_and_hsdp_layer_full():
     g0, m0 = SM.hier_fold_starts(pos, count, S, R, "ring")
     want = SM.hier_reduce_positions(vals, S, g0, m0, "bf16", "avg", "bf16")
     assert_same(_gather(recv[5], pos), want, "bf16", "two-level all-reduce")
-    del send, recv
+    del send, recv, arena                                     # release the first arena before the second
     torch.cuda.empty_cache()
 
     numels = [n for _, n in fsdp_layer_tensors()]
