@@ -62,7 +62,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--layout", default="arena", choices=["arena", "staggered", "separate"],
                    help="placement of the rank buffers in HBM")
-    p.add_argument("--stagger", type=int, default=4096, help="extra bytes between consecutive ranks' memory")
+    p.add_argument("--stagger", type=int, default=None,
+                   help="extra bytes between consecutive ranks' memory (default: the workload's, else 4096)")
     p.add_argument("--max-region", type=int, default=32, metavar="GIB",
                    help="largest per-rank region of the rank arena (a power of two, GiB)")
     p.add_argument("--seed", type=int, default=0)
@@ -117,19 +118,20 @@ class Layout:
     """Where the N rank buffers of a workload live in HBM.
 
     arena      (default) each rank owns one region of HBM (RankArena: regions a
-               large power of two apart, 4 KiB stagger); every buffer of rank r
+               large power of two apart plus a stagger, 4 KiB unless the workload
+               names its own); every buffer of rank r
                is carved from region r, as a real rank's buffers sit in its GPU
     staggered  one allocation per buffer set, ranks 4 KiB apart (gc_rank_buffers)
     separate   one torch allocation per rank buffer
     """
 
-    def __init__(self, args, nranks):
+    def __init__(self, args, nranks, stagger=None):
         import collective_communication_reduction_amd as gc
         self.gc = gc
         self.kind = args.layout
         self.nranks = nranks
-        self.stagger = args.stagger
-        self.arena = (gc.RankArena(nranks, stagger_bytes=args.stagger, max_region=args.max_region << 30)
+        self.stagger = args.stagger if args.stagger is not None else (stagger or 4096)
+        self.arena = (gc.RankArena(nranks, stagger_bytes=self.stagger, max_region=args.max_region << 30)
                       if self.kind == "arena" else None)
 
     def buffers(self, count, tdt):
@@ -462,7 +464,7 @@ class HierWorkload(Workload):
         self.cfg = cfg
         self.N, self.S, self.count = cfg["nranks"], cfg["group"], cfg["count"]
         self.name = "hier_ar_n16"
-        L = Layout(args, self.N)
+        L = Layout(args, self.N, stagger=cfg.get("stagger"))
         self.layout = L.name()
         self.send = L.buffers(self.count, torch.bfloat16)
         self.recv = L.buffers(self.count, torch.bfloat16)

@@ -58,7 +58,10 @@ WORKLOADS = {
                         cap_bytes=25 * 1024 * 1024),
     "fsdp_layer_n64": dict(nranks=64, dtype="bf16", grad_sigma=1e-3, param_sigma=0.02),
     "fsdp2_layer_n64": dict(nranks=64, dtype="bf16", grad_sigma=1e-3, param_sigma=0.02),
-    "hier_ar_n16": dict(nranks=16, group=8, count=33_554_432, dtype="bf16", op="avg", sigma=1e-3),
+    # 64 KiB between consecutive ranks' regions: measured 6.31 TB/s against 6.04 with 4 KiB for this
+    # 16-rank layout (8- and 64-rank layouts keep 4 KiB: 64 KiB was equal or up to 2.7 % slower there)
+    "hier_ar_n16": dict(nranks=16, group=8, count=33_554_432, dtype="bf16", op="avg", sigma=1e-3,
+                        stagger=65536),
     "hsdp_layer_n16": dict(nranks=16, group=8, dtype="bf16", grad_sigma=1e-3),
     "moe_a2a_n8": dict(nranks=8, tokens=16384, hidden=4096, experts=64, topk=2, zipf_s=1.1),
     "moe_ep_n8": dict(nranks=8, tokens=16384, hidden=4096, experts=64, topk=2, zipf_s=1.1, dtype="bf16"),

@@ -1,6 +1,6 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration and
 HBM layout bench.py times (a RankArena: each rank's buffers in its own region
-of HBM, 4 KiB stagger between ranks).
+of HBM, the workload's stagger between ranks: 4 KiB, 64 KiB for 16 ranks).
 
 At these sizes the step-by-step oracle cannot hold the inputs, so each test
 checks (a) sampled outputs the oracle computes one by one from inputs it
@@ -479,7 +479,7 @@ def test_hier_ar_n16_and_hsdp_layer_full():
     N, S, count = cfg["nranks"], cfg["group"], cfg["count"]
     R = N // S
     keys = [G.stream_key(SEED, r, 0) for r in range(N)]
-    arena = gc.RankArena(N)
+    arena = gc.RankArena(N, stagger_bytes=cfg["stagger"])          # the layout bench.py times
     send = arena.alloc(count, "bf16")
     for r in range(N):
         GD.fill_normal_bf16(send[r], keys[r], cfg["sigma"])
