@@ -763,7 +763,7 @@ def _quantile(xs, q):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs all N ranks as buffers in one MI355X's HBM "
+        print(f"bench.py measures one GPU: the library runs all N ranks as buffers in one MI355X's HBM "
               f"(no collectives across GPUs), so --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
     import torch
