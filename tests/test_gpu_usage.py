@@ -44,10 +44,11 @@ def test_usage_example():
     plan.close()
 
     E, K, T, H = 2, 2, 1000, 512                             # MoE: 2 experts per rank, top-2
-    experts = [torch.randint(0, N * E, (T, K), dtype=torch.int32, device="cuda") for _ in range(N)]
+    rng = torch.Generator(device="cuda").manual_seed(7)
+    experts = [torch.randint(0, N * E, (T, K), dtype=torch.int32, device="cuda", generator=rng) for _ in range(N)]
     for e in experts:
         e[:, 1] = (e[:, 0] + 1) % (N * E)                    # two distinct experts per token
-    tokens = [torch.randn(T, H, device="cuda").bfloat16() for _ in range(N)]
+    tokens = [torch.randn(T, H, device="cuda", generator=rng).bfloat16() for _ in range(N)]
     splits = torch.empty(N * N * E, dtype=torch.int64, device="cuda")
     dest = [torch.empty(T * K * 2, dtype=torch.int32, device="cuda") for _ in range(N)]
     scratch = torch.empty(gc.gc_moe_route_scratch_bytes([T] * N, K, E), dtype=torch.uint8, device="cuda")
