@@ -451,6 +451,10 @@ def test_device_generator_matches_host():
         assert np.array_equal(from_dev(t), G.normal_bf16(key, np.arange(n) + 5, 1e-3))
         t = GD.fill_int32(torch.empty(n, dtype=torch.int32, device=DEV), key)
         assert np.array_equal(t.cpu().numpy(), G.int32_values(key, np.arange(n)))
+        big = (1 << 32) + 17                                 # element indices past 2^32
+        t = GD.fill_normal_f32(torch.empty(n, dtype=torch.float32, device=DEV), key, 0.5, base=big)
+        want = G.normal_f32(key, np.arange(n, dtype=np.uint64) + np.uint64(big), 0.5)
+        assert np.array_equal(t.cpu().numpy().view(np.uint32), np.asarray(want, dtype=np.float32).view(np.uint32))
     tokens = np.array([5, 0, 77, 5, 1023], dtype=np.int32)
     H = 96
     key = G.stream_key(0, 2, 0)
