@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--workload", default="ar_bf16_n8",
                    choices=["ar_bf16_n8", "ar_fp32_n4", "ddp_llama7b", "ddp_llama7b_zero_copy", "fsdp_layer_n64",
                             "moe_a2a_n8", "moe_ep_n8", "fsdp2_layer_n64", "hier_ar_n16"])
+    p.add_argument("--algo", default="fused", choices=["fused", "rs_ag"],
+                   help="all-reduce workloads: fused single pass, or reduce-scatter to a scratch shard then all-gather")
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--layout", default="arena", choices=["arena", "staggered", "separate"],
                    help="placement of the rank buffers in HBM")
@@ -164,10 +166,16 @@ class AllReduceWorkload(Workload):
         self.N, self.S, self.dtype, self.op = nranks, count, dtype, op
         tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
         es = 2 if dtype == "bf16" else 4
-        self.name = f"ar_{dtype}_n{nranks}"
-        self.bytes_per_step = 2 * nranks * count * es
-        self.dominant = "reduce_vec_kernel (fused all-reduce)"
+        self.algo = args.algo
+        self.name = f"ar_{dtype}_n{nranks}" + ("" if self.algo == "fused" else "_rs_ag")
+        self.bytes_per_step = 2 * nranks * count * es          # the all-reduce's own bytes, either algorithm
+        self.dominant = ("reduce_vec_kernel (fused all-reduce)" if self.algo == "fused" else
+                         "reduce_vec_kernel (reduce-scatter to scratch) + gather_vec_kernel (all-gather)")
         self.dominant_bytes = self.bytes_per_step
+        self.scratch = None
+        if self.algo == "rs_ag":
+            self.scratch = torch.empty(max(1, gc.gc_all_reduce_scratch_bytes(count, nranks, dtype, "rs_ag")),
+                                       dtype=torch.uint8, device="cuda")
         self.sets = []
         L = Layout(args, nranks)
         self.layout = L.name()
@@ -190,12 +198,12 @@ class AllReduceWorkload(Workload):
 
     def step(self, k):
         sp, rp = self.ptrs[k % len(self.ptrs)]
-        self.gc.gc_all_reduce(sp, rp, op=self.op, order="ring", algo="fused", count=self.S, dtype=self.dtype,
-                              stream=self.stream)
+        self.gc.gc_all_reduce(sp, rp, op=self.op, order="ring", algo=self.algo, scratch=self.scratch,
+                              count=self.S, dtype=self.dtype, stream=self.stream)
 
     def config(self):
         return {"workload": self.name, "nranks": self.N, "count_per_rank": self.S, "storage": self.dtype,
-                "op": self.op, "order": "ring", "algo": "fused", "replicas": len(self.sets), "layout": self.layout}
+                "op": self.op, "order": "ring", "algo": self.algo, "replicas": len(self.sets), "layout": self.layout}
 
     def cpu_sample(self, seed):
         """Oracle all-reduce on the first quarter of every rank's buffer."""
