@@ -61,6 +61,8 @@ def parse():
                             "moe_a2a_n8", "moe_ep_n8", "fsdp2_layer_n64", "hier_ar_n16"])
     p.add_argument("--algo", default="fused", choices=["fused", "rs_ag"],
                    help="all-reduce workloads: fused single pass, or reduce-scatter to a scratch shard then all-gather")
+    p.add_argument("--order", default="ring", choices=["ring", "rank", "ring_wire"],
+                   help="all-reduce workloads: fold order (ring; rank 0..N-1; ring with bf16 partials on the wire)")
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--layout", default="arena", choices=["arena", "staggered", "separate"],
                    help="placement of the rank buffers in HBM")
@@ -167,7 +169,9 @@ class AllReduceWorkload(Workload):
         tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
         es = 2 if dtype == "bf16" else 4
         self.algo = args.algo
-        self.name = f"ar_{dtype}_n{nranks}" + ("" if self.algo == "fused" else "_rs_ag")
+        self.order = args.order
+        self.name = (f"ar_{dtype}_n{nranks}" + ("" if self.algo == "fused" else "_rs_ag") +
+                     ("" if self.order == "ring" else f"_{self.order}"))
         self.bytes_per_step = 2 * nranks * count * es          # the all-reduce's own bytes, either algorithm
         self.dominant = ("reduce_vec_kernel (fused all-reduce)" if self.algo == "fused" else
                          "reduce_vec_kernel (reduce-scatter to scratch) + gather_vec_kernel (all-gather)")
@@ -198,12 +202,12 @@ class AllReduceWorkload(Workload):
 
     def step(self, k):
         sp, rp = self.ptrs[k % len(self.ptrs)]
-        self.gc.gc_all_reduce(sp, rp, op=self.op, order="ring", algo=self.algo, scratch=self.scratch,
+        self.gc.gc_all_reduce(sp, rp, op=self.op, order=self.order, algo=self.algo, scratch=self.scratch,
                               count=self.S, dtype=self.dtype, stream=self.stream)
 
     def config(self):
         return {"workload": self.name, "nranks": self.N, "count_per_rank": self.S, "storage": self.dtype,
-                "op": self.op, "order": "ring", "algo": self.algo, "replicas": len(self.sets), "layout": self.layout}
+                "op": self.op, "order": self.order, "algo": self.algo, "replicas": len(self.sets), "layout": self.layout}
 
     def cpu_sample(self, seed):
         """Oracle all-reduce on the first quarter of every rank's buffer."""
