@@ -19,8 +19,11 @@ same way; the zero-copy DDP step all-reduces each bucket in place over the
 gradient tensors instead of packing and unpacking it), and moe_ep_n8 (the
 expert-parallel MoE data flow: routing plan, dispatch from token order and
 weighted combine back to token order, identity experts), and fsdp2_layer_n64
-(the FSDP layer sharded per parameter on dim 0, as FSDP2 does), and hier_ar_n16
-(the two-level all-reduce of 16 ranks as two groups of eight).
+(the FSDP layer sharded per parameter on dim 0, as FSDP2 does), hier_ar_n16
+(the two-level all-reduce of 16 ranks as two groups of eight), and hsdp_layer_n16
+(the HSDP step of the same layer on that mesh: reduce-scatter over all 16 ranks,
+all-gather inside each group).  --algo rs_ag and --order rank / ring_wire time the
+all-reduce workloads' other algorithm and fold orders.
 """
 
 import argparse
@@ -48,7 +51,8 @@ KERNEL_SOURCES = {
 }
 WORKLOAD_KERNELS = {"ar_bf16_n8": "reduce", "ar_fp32_n4": "reduce", "ddp_llama7b": "reduce",
                     "fsdp_layer_n64": "reduce", "ddp_llama7b_zero_copy": "bucket", "moe_a2a_n8": "a2a",
-                    "moe_ep_n8": "moe", "fsdp2_layer_n64": "reduce", "hier_ar_n16": "hier"}
+                    "moe_ep_n8": "moe", "fsdp2_layer_n64": "reduce", "hier_ar_n16": "hier",
+                    "hsdp_layer_n16": "hier"}
 
 
 def parse():
@@ -58,7 +62,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ar_bf16_n8",
                    choices=["ar_bf16_n8", "ar_fp32_n4", "ddp_llama7b", "ddp_llama7b_zero_copy", "fsdp_layer_n64",
-                            "moe_a2a_n8", "moe_ep_n8", "fsdp2_layer_n64", "hier_ar_n16"])
+                            "moe_a2a_n8", "moe_ep_n8", "fsdp2_layer_n64", "hier_ar_n16", "hsdp_layer_n16"])
     p.add_argument("--algo", default="fused", choices=["fused", "rs_ag"],
                    help="all-reduce workloads: fused single pass, or reduce-scatter to a scratch shard then all-gather")
     p.add_argument("--order", default="ring", choices=["ring", "rank", "ring_wire"],
@@ -509,6 +513,75 @@ class HierWorkload(Workload):
         return run, 2 * self.N * m * 2, f"oracle three-ring two-level all-reduce of 16 ranks x {m} bf16"
 
 
+class HsdpWorkload(Workload):
+    """HSDP step of one transformer layer on 16 ranks as 2 groups of 8 (two nodes of eight GPUs): the gradient
+    reduce-scatter (avg, bf16 -> fp32) over all 16 ranks, member i of every group keeping shard i, then the
+    all-gather of the bf16 parameter shards inside each group."""
+
+    def __init__(self, args):
+        import torch
+        import collective_communication_reduction_amd as gc
+        from gen import device as GD
+        from gen.workloads import WORKLOADS, fsdp_layer_tensors
+        self.gc = gc
+        cfg = WORKLOADS["hsdp_layer_n16"]
+        self.N, self.G = cfg["nranks"], cfg["group"]
+        self.R = self.N // self.G
+        self.name = "hsdp_layer_n16"
+        total = sum(n for _, n in fsdp_layer_tensors())
+        self.S = -(-total // self.G) * self.G
+        self.rc = self.S // self.G
+        L = Layout(args, self.N, stagger=cfg.get("stagger"))
+        self.grads = L.buffers(self.S, torch.bfloat16)
+        self.gshards = L.buffers(self.rc, torch.float32)
+        self.pshards = L.buffers(self.rc, torch.bfloat16)
+        self.params = L.buffers(self.S, torch.bfloat16)
+        self.layout = L.name()
+        for r in range(self.N):
+            GD.fill_normal_bf16(self.grads[r], _keyed(args.seed, r, 0), cfg["grad_sigma"])
+            GD.fill_normal_bf16(self.pshards[r], _keyed(args.seed, r % self.G, 1), 0.02)
+        self.gp, self.sp = gc.gc_pointers(self.grads), gc.gc_pointers(self.gshards)
+        groups = [range(g * self.G, (g + 1) * self.G) for g in range(self.R)]
+        self.agp = [(gc.gc_pointers([self.pshards[r] for r in m]), gc.gc_pointers([self.params[r] for r in m]))
+                    for m in groups]
+        self.rs_bytes = self.N * self.S * 2 + self.N * self.rc * 4
+        self.ag_bytes = self.N * self.rc * 2 + self.N * self.S * 2
+        self.bytes_per_step = self.rs_bytes + self.ag_bytes
+        self.dominant = "hier_vec_kernel (HSDP reduce-scatter, 2 x 8 ranks)"
+        self.dominant_bytes = self.rs_bytes
+        torch.cuda.synchronize()
+
+    def rs(self):
+        self.gc.gc_hsdp_reduce_scatter(self.gp, self.sp, self.G, op="avg", order="ring", recv_count=self.rc,
+                                       in_dtype="bf16", out_dtype="fp32")
+
+    def step(self, k):
+        self.rs()
+        for pin, pout in self.agp:
+            self.gc.gc_all_gather(pin, pout, count=self.rc, dtype="bf16")
+
+    def dominant_launch(self, k):
+        self.rs()
+
+    def config(self):
+        return {"workload": self.name, "nranks": self.N, "groups": self.R, "group_size": self.G,
+                "flat_numel": self.S, "shard": self.rc, "rs": "bf16->fp32 avg, two-level ring",
+                "ag": "bf16 inside each group", "layout": self.layout}
+
+    def cpu_sample(self, seed):
+        import numpy as np
+        from gen import host as G
+        from oracle import sampled as SM
+        m, i = 1 << 16, 3                     # 65536 sampled outputs of member 3 (every group holds them)
+        p = i * self.rc + np.arange(m)
+        vals = np.stack([G.normal_bf16(_keyed(seed, r, 0), p, 1e-3) for r in range(self.N)])
+
+        def run():
+            g0, m0 = SM.hier_fold_starts(p, self.S, self.G, self.R, "ring", chunk=self.rc)
+            return SM.hier_reduce_positions(vals, self.G, g0, m0, "bf16", "avg", "fp32")
+        return run, self.N * m * 2 + m * 4, f"oracle two-level fold of {m} outputs of member {i} (16-way each)"
+
+
 class MoeWorkload(Workload):
     """MoE dispatch all-to-all, 8 ranks x 16384 tokens x 4096 bf16, top-2 of 64 experts, Zipf(1.1)."""
 
@@ -682,6 +755,8 @@ def make(args):
         return Fsdp2Workload(args)
     if args.workload == "hier_ar_n16":
         return HierWorkload(args)
+    if args.workload == "hsdp_layer_n16":
+        return HsdpWorkload(args)
     return MoeWorkload(args)
 
 

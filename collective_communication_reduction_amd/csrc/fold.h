@@ -64,6 +64,33 @@ __device__ __forceinline__ void put(char* p, const Words<Out, VE>& r) {
   }
 }
 
+// Results of 32 bytes per lane (eight fp32 from eight bf16 inputs) regrouped
+// so that each of a wavefront's two store instructions writes 1 KiB
+// contiguously.  Lane l holds vector vw + l of the wavefront (vw its first);
+// half h of the result, for lane l, is half (l & 1) of vector vw + 32 h + l/2,
+// fetched from that lane with ds_bpermute, and goes to byte 1024 h + 16 l of
+// the wavefront's 2 KiB.  Stored per lane as two 16-byte halves of its own
+// 32 bytes, each instruction wrote every other 16 bytes: lines then left L2
+// half written and were written back twice (14 % more write traffic).  Every
+// lane of the wavefront must execute this (cross-lane reads).
+template <class Out, int VE>
+__device__ __forceinline__ void wave_halves32(const Words<Out, VE>& w, u32x4& h0, u32x4& h1) {
+  static_assert(Words<Out, VE>::NW == 8, "32-byte results per lane");
+  const uint32_t lane = threadIdx.x & 63;
+  u32x4 h[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int src = static_cast<int>((32 * half + (lane >> 1)) << 2);
+    uint32_t x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      x[k] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(w.w[k])));
+    h[half] = (lane & 1) ? u32x4{x[4], x[5], x[6], x[7]} : u32x4{x[0], x[1], x[2], x[3]};
+  }
+  h0 = h[0];
+  h1 = h[1];
+}
+
 __device__ __forceinline__ uint32_t next_rank(uint32_t r, uint32_t N) { return r + 1 == N ? 0 : r + 1; }
 
 // A partial as the ring forwards it when WIRE is set: rounded to the input's

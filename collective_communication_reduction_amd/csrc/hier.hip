@@ -130,7 +130,21 @@ __device__ __forceinline__ void hier_tile(const HierArgs<P>& a, const char* cons
     for (int l = 0; l < VE; ++l) o[l] = finish(acc[u][l], avg, a.nf);
     const Words<Out, VE> w = pack<Out, VE>(o);
     const uint64_t e0 = a.phase + v * VE;
-    if (!GUARD || v < c.vhi) {
+    if constexpr (KIND == kHsdpReduceScatter && Words<Out, VE>::NW == 8) {
+      // bf16 -> fp32: 1 KiB lane-contiguous stores to every holder (all lanes take part)
+      const uint32_t lane = threadIdx.x & 63;
+      const uint64_t vw = v - lane;
+      u32x4 h0, h1;
+      wave_halves32<Out, VE>(w, h0, h1);
+      const bool ok0 = !GUARD || vw + (lane >> 1) < c.vhi;
+      const bool ok1 = !GUARD || vw + 32 + (lane >> 1) < c.vhi;
+      const uint64_t off = (a.phase + vw * VE - c.clo) * Out::ES;
+      for (uint32_t g = 0; g < a.R; ++g) {
+        char* base = a.out[g * a.S + i] + off;
+        if (ok0) st16(base + 16 * lane, h0);
+        if (ok1) st16(base + 1024 + 16 * lane, h1);
+      }
+    } else if (!GUARD || v < c.vhi) {
       if constexpr (KIND == kHierAllReduce) {
         for (uint32_t q = 0; q < a.N; ++q) put<Out, VE>(a.out[q] + e0 * Out::ES, w);
       } else {

@@ -109,7 +109,16 @@ __device__ __forceinline__ void reduce_tile(const RedArgs<P>& a, uint32_t N, uin
     for (int l = 0; l < VE; ++l) o[l] = finish(acc[u][l], avg, a.nf);
     const Words<Out, VE> w = pack<Out, VE>(o);
     const uint64_t e0 = a.phase + v * VE;
-    if (!GUARD || v < g.vhi) {
+    if constexpr (KIND == kReduceScatter && Words<Out, VE>::NW == 8) {
+      // bf16 -> fp32: 1 KiB lane-contiguous stores (every lane takes part in the regrouping)
+      const uint32_t lane = threadIdx.x & 63;
+      const uint64_t vw = v - lane;
+      u32x4 h0, h1;
+      wave_halves32<Out, VE>(w, h0, h1);
+      char* base = a.out[j] + (a.phase + vw * VE - g.lo) * Out::ES;
+      if (!GUARD || vw + (lane >> 1) < g.vhi) st16(base + 16 * lane, h0);
+      if (!GUARD || vw + 32 + (lane >> 1) < g.vhi) st16(base + 1024 + 16 * lane, h1);
+    } else if (!GUARD || v < g.vhi) {
       if constexpr (KIND == kAllReduce) {
         for (uint32_t q = 0; q < N; ++q) put<Out, VE>(a.out[q] + e0 * Out::ES, w);
       } else {

@@ -509,7 +509,7 @@ def test_hier_ar_n16_and_hsdp_layer_full():
     numels = [n for _, n in fsdp_layer_tensors()]
     _, _, Sflat, _ = OB.flat_param_shards(numels, S)
     rc = Sflat // S
-    arena = gc.RankArena(N)
+    arena = gc.RankArena(N, stagger_bytes=WORKLOADS["hsdp_layer_n16"]["stagger"])
     grads = arena.alloc(Sflat, "bf16")
     for r in range(N):
         GD.fill_normal_bf16(grads[r], keys[r], 1e-3)
