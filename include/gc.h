@@ -16,9 +16,12 @@
  *     split tables and size lists are HOST arrays, read before the call returns.
  *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *     without synchronising; results are visible to later work on that stream.
- *   - Arguments are validated on the host first.  A status other than GC_OK
- *     means nothing was enqueued.  GC_ERR_HIP means a launch failed; faults
- *     inside a kernel surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host first: GC_ERR_INVALID_ARG and
+ *     GC_ERR_UNSUPPORTED mean nothing was enqueued.  GC_ERR_HIP means a launch
+ *     failed; a call that issues several launches (one per parameter, per
+ *     batch of segments, per phase) may have enqueued the ones before it, so
+ *     its outputs are then incomplete.  Faults inside a kernel surface at the
+ *     caller's next synchronisation.
  *   - No call allocates device memory.  The bucket plan is a host object.
  *   - No call memsets, copies through the host or synchronises, so calls can
  *     be captured into a HIP graph and replayed (validation runs at capture).
