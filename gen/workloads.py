@@ -1,4 +1,4 @@
-"""Shapes and synthetic-input recipes of the five gradient-sync workloads.
+"""Shapes and synthetic-input recipes of the gradient-sync workloads.
 
 Shapes only, plus the MoE routing draw (an input: which expert each token is
 sent to).  No collective arithmetic and no bucket layout live here.
@@ -10,8 +10,15 @@ sent to).  No collective arithmetic and no bucket layout live here.
   fsdp_layer_n64  FSDP unit step on one transformer layer (202,383,360 params),
                   64 ranks: reduce-scatter (avg) bf16 -> fp32 shards, then
                   all-gather of bf16 parameter shards normal(0,0.02)
+  fsdp2_layer_n64 the same layer with per-parameter dim-0 shards (FSDP2)
+  hier_ar_n16     two-level all-reduce (avg), 16 ranks in groups of 8,
+                  33,554,432 bf16 each, normal(0,1e-3)
+  hsdp_layer_n16  HSDP step on the layer: 16 ranks in groups of 8, gradient
+                  reduce-scatter (avg) bf16 -> fp32 over all 16 ranks with member
+                  i of each group keeping shard i, then all-gather in each group
   moe_a2a_n8      MoE dispatch all-to-all, 8 ranks x 16384 tokens x 4096 bf16
                   normal(0,1), top-2 of 64 experts (8 per rank), Zipf(1.1)
+  moe_ep_n8       the same tokens and routing through route -> dispatch -> combine
 
 Key of rank r's data in every workload: stream_key(seed, r, stream).
 """
