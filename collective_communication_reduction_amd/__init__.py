@@ -3,7 +3,10 @@
 A thin ctypes layer over the C ABI declared in include/gc.h.  It only marshals
 arguments: it turns lists of tensors (or raw device addresses) into pointer
 arrays, maps dtype/op/order names onto the C enums, passes torch's current HIP
-stream, and raises GcError for a non-OK status.  Every collective runs in the
+stream, and raises GcError for a non-OK status.  Since the library sees only
+addresses, a tensor is checked here first (a contiguous device tensor that
+holds every byte the call touches, else ValueError); raw addresses and
+gc_pointers arrays are the caller's responsibility.  Every collective runs in the
 HIP kernels of libgc.so; there is no other implementation to fall back to, and
 importing this package fails if the library has not been built
 (python collective_communication_reduction_amd/build.py).
@@ -121,23 +124,44 @@ def _check(status, what):
 
 # ------------------------------------------------------------------ marshalling
 
-def _addr(x):
-    """Device address of a tensor (data_ptr) or a raw integer address; None -> NULL."""
-    if x is None:
-        return None
-    if isinstance(x, int):
+_ES = {GC_INT32: 4, GC_FP32: 4, GC_BF16: 2}
+
+
+def _buf(x, nbytes, what):
+    """Address of one device buffer that a call reads or writes for nbytes bytes.
+
+    A tensor must be a contiguous device tensor of at least nbytes bytes: the C
+    ABI sees only its address, so a host, strided or short tensor would reach the
+    kernels as an out-of-bounds access.  A raw integer address (or None) is the
+    caller's responsibility and passes unchecked."""
+    if x is None or isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError(f"{what}: a device (cuda) tensor is required")
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: the tensor is not contiguous")
+    have = x.numel() * x.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what}: {have} bytes, the call touches {nbytes}")
     return x.data_ptr()
 
 
-def _ptr_array(xs):
+def _bufs(xs, n, nbytes, what):
+    """Pointer array of the first n buffers of xs, each checked by _buf.
+
+    nbytes is one size for every buffer or a sequence with one size per buffer.
+    A pointer array made by gc_pointers passes unchecked but must hold n
+    entries; None passes as NULL (the library rejects it)."""
     if xs is None:
         return None
-    if isinstance(xs, ctypes.Array):     # already marshalled (gc_pointers)
+    if len(xs) < n:
+        raise ValueError(f"{what}: {len(xs)} buffers, the call needs {n}")
+    if isinstance(xs, ctypes.Array):
         return xs
     arr = (ctypes.c_void_p * max(1, len(xs)))()
     for i, x in enumerate(xs):
-        arr[i] = _addr(x)
+        need = nbytes if isinstance(nbytes, int) else (int(nbytes[i]) if i < n else 0)
+        arr[i] = _buf(x, need if i < n else 0, f"{what}[{i}]")
     return arr
 
 
@@ -159,8 +183,11 @@ def gc_pointers(tensors):
 
     Every call that takes a list also accepts the returned array, which saves
     rebuilding it when the same buffers are synchronised every step (DDP's
-    gradient tensors persist across steps)."""
-    return _ptr_array(list(tensors))
+    gradient tensors persist across steps).  Tensors must be contiguous device
+    tensors; their sizes are not known here, so the calls that take the array
+    trust it."""
+    xs = list(tensors)
+    return _bufs(xs, len(xs), 0, "gc_pointers")
 
 
 def _stream(stream, like=None):
@@ -210,8 +237,10 @@ def gc_all_reduce(send, recv=None, op="avg", order="ring", algo="fused", scratch
     a = _enum(_ALGO, algo)
     if scratch_bytes is None:
         scratch_bytes = scratch.numel() * scratch.element_size() if hasattr(scratch, "numel") else 0
-    _check(_c_ar(_ptr_array(send), _ptr_array(recv), cnt, n, t, _enum(_OP, op), _enum(_ORDER, order), a,
-                 _addr(scratch), int(scratch_bytes), _stream(stream, _first(send))), "gc_all_reduce")
+    nb = cnt * _ES.get(t, 0)
+    _check(_c_ar(_bufs(send, n, nb, "send"), _bufs(recv, n, nb, "recv"), cnt, n, t, _enum(_OP, op),
+                 _enum(_ORDER, order), a, _buf(scratch, int(scratch_bytes), "scratch"), int(scratch_bytes),
+                 _stream(stream, _first(send))), "gc_all_reduce")
     return recv
 
 
@@ -226,8 +255,9 @@ def gc_reduce_scatter(send, recv, op="avg", order="ring", recv_count=None, in_dt
     ti = _infer_dtype(send, in_dtype)
     to = _infer_dtype(recv, out_dtype)
     rc = _numel(recv, recv_count)
-    _check(_c_rs(_ptr_array(send), _ptr_array(recv), rc, n, ti, to, _enum(_OP, op), _enum(_ORDER, order),
-                 _stream(stream, _first(send))), "gc_reduce_scatter")
+    _check(_c_rs(_bufs(send, n, n * rc * _ES.get(ti, 0), "send"), _bufs(recv, n, rc * _ES.get(to, 0), "recv"), rc,
+                 n, ti, to, _enum(_OP, op), _enum(_ORDER, order), _stream(stream, _first(send))),
+           "gc_reduce_scatter")
     return recv
 
 
@@ -236,7 +266,9 @@ def gc_all_gather(send, recv, count=None, dtype=None, stream=None):
     n = len(send)
     t = _infer_dtype(send, dtype)
     cnt = _numel(send, count)
-    _check(_c_ag(_ptr_array(send), _ptr_array(recv), cnt, n, t, _stream(stream, _first(send))), "gc_all_gather")
+    nb = cnt * _ES.get(t, 0)
+    _check(_c_ag(_bufs(send, n, nb, "send"), _bufs(recv, n, n * nb, "recv"), cnt, n, t,
+                 _stream(stream, _first(send))), "gc_all_gather")
     return recv
 
 
@@ -247,17 +279,23 @@ def gc_all_to_all(send, recv, splits, row_bytes, stream=None):
     if sp.ndim != 3:
         raise ValueError("splits must be [N][N][E]")
     n, _, e = sp.shape
-    _check(_c_a2a(_ptr_array(send), _ptr_array(recv), sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, e,
-                  int(row_bytes), _stream(stream, _first(send))), "gc_all_to_all")
+    rb = int(row_bytes)
+    rows_out = [max(0, int(x)) * rb for x in sp.clip(min=0).sum(axis=(1, 2))] if n else []
+    rows_in = [max(0, int(x)) * rb for x in sp.clip(min=0).sum(axis=(0, 2))] if n else []
+    _check(_c_a2a(_bufs(send, n, rows_out, "send"), _bufs(recv, n, rows_in, "recv"),
+                  sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, e, rb, _stream(stream, _first(send))),
+           "gc_all_to_all")
     return recv
 
 
 def gc_hier_all_reduce(send, recv, group_size, op="avg", order="ring", count=None, dtype=None, stream=None):
     """Two-level all-reduce over len(send) = R * group_size ranks (member i of group g = rank g*group_size + i)."""
     n = len(send)
-    _check(_c_hier_ar(_ptr_array(send), _ptr_array(recv), _numel(send, count), n, int(group_size),
-                      _infer_dtype(send, dtype), _enum(_OP, op), _enum(_ORDER, order), _stream(stream, _first(send))),
-           "gc_hier_all_reduce")
+    t = _infer_dtype(send, dtype)
+    cnt = _numel(send, count)
+    nb = cnt * _ES.get(t, 0)
+    _check(_c_hier_ar(_bufs(send, n, nb, "send"), _bufs(recv, n, nb, "recv"), cnt, n, int(group_size), t,
+                      _enum(_OP, op), _enum(_ORDER, order), _stream(stream, _first(send))), "gc_hier_all_reduce")
     return recv
 
 
@@ -268,8 +306,10 @@ def gc_hsdp_reduce_scatter(send, recv, group_size, op="avg", order="ring", recv_
     rc = int(recv_count) if recv_count is not None else int(recv[0].numel())
     tin = _infer_dtype(send, in_dtype)
     tout = _infer_dtype(recv, out_dtype)
-    _check(_c_hsdp_rs(_ptr_array(send), _ptr_array(recv), rc, n, int(group_size), tin, tout, _enum(_OP, op),
-                      _enum(_ORDER, order), _stream(stream, _first(send))), "gc_hsdp_reduce_scatter")
+    g = max(0, int(group_size))
+    _check(_c_hsdp_rs(_bufs(send, n, g * rc * _ES.get(tin, 0), "send"), _bufs(recv, n, rc * _ES.get(tout, 0), "recv"),
+                      rc, n, int(group_size), tin, tout, _enum(_OP, op), _enum(_ORDER, order),
+                      _stream(stream, _first(send))), "gc_hsdp_reduce_scatter")
     return recv
 
 
@@ -279,42 +319,54 @@ def _sz_array(xs):
 
 
 def _rank_major(xs, nranks, nparams):
-    """Accept [rank][param] nested lists, a flat rank-major list, or a marshalled array."""
+    """Accept [rank][param] nested lists or a flat rank-major list (returned flat), or a marshalled array."""
     if isinstance(xs, ctypes.Array):
         return xs
     if len(xs) == nranks and nparams and isinstance(xs[0], (list, tuple)):
         xs = [x for row in xs for x in row]
     if len(xs) != nranks * nparams:
         raise ValueError("need nranks * nparams pointers")
-    return _ptr_array(xs)
+    return xs
+
+
+def _shard_bytes(rows, cols, nranks, es):
+    """Bytes of every (rank, parameter) dim-0 shard, rank-major (torch.chunk's rule)."""
+    out = []
+    for r in range(nranks):
+        for nr, nc in zip(rows, cols):
+            c = -(-int(nr) // nranks)
+            out.append((min(int(nr), (r + 1) * c) - min(int(nr), r * c)) * int(nc) * es)
+    return out
 
 
 def gc_fsdp2_reduce_scatter(grads, shards, rows, cols, nranks, in_dtype, out_dtype=None, op="avg", order="ring",
                             stream=None):
     """Per-parameter Shard(0) reduce-scatter; grads / shards as [rank][param] (or flat rank-major)."""
-    P = len(rows)
+    P, N = len(rows), int(nranks)
     out_dtype = in_dtype if out_dtype is None else out_dtype
-    g = _rank_major(grads, nranks, P)
-    sh = _rank_major(shards, nranks, P)
-    like = None if isinstance(grads, ctypes.Array) else _first([x for row in grads for x in row]
-                                                                if grads and isinstance(grads[0], (list, tuple))
-                                                                else grads)
-    _check(_c_fsdp2_rs(g, sh, _sz_array(rows), _sz_array(cols), P, int(nranks), _dtype_code(in_dtype),
-                       _dtype_code(out_dtype), _enum(_OP, op), _enum(_ORDER, order), _stream(stream, like)),
+    ti, to = _dtype_code(in_dtype), _dtype_code(out_dtype)
+    g = _rank_major(grads, N, P)
+    sh = _rank_major(shards, N, P)
+    full = [int(nr) * int(nc) * _ES.get(ti, 0) for nr, nc in zip(rows, cols)] * max(N, 0)
+    part = _shard_bytes(rows, cols, N, _ES.get(to, 0)) if N > 0 else []
+    like = None if isinstance(g, ctypes.Array) else _first(g)
+    _check(_c_fsdp2_rs(_bufs(g, N * P, full, "grads"), _bufs(sh, N * P, part, "shards"), _sz_array(rows),
+                       _sz_array(cols), P, N, ti, to, _enum(_OP, op), _enum(_ORDER, order), _stream(stream, like)),
            "gc_fsdp2_reduce_scatter")
     return shards
 
 
 def gc_fsdp2_all_gather(shards, params, rows, cols, nranks, dtype, stream=None):
     """Per-parameter Shard(0) all-gather; shards / params as [rank][param] (or flat rank-major)."""
-    P = len(rows)
-    sh = _rank_major(shards, nranks, P)
-    pa = _rank_major(params, nranks, P)
-    like = None if isinstance(params, ctypes.Array) else _first([x for row in params for x in row]
-                                                                 if params and isinstance(params[0], (list, tuple))
-                                                                 else params)
-    _check(_c_fsdp2_ag(sh, pa, _sz_array(rows), _sz_array(cols), P, int(nranks), _dtype_code(dtype),
-                       _stream(stream, like)), "gc_fsdp2_all_gather")
+    P, N = len(rows), int(nranks)
+    t = _dtype_code(dtype)
+    sh = _rank_major(shards, N, P)
+    pa = _rank_major(params, N, P)
+    full = [int(nr) * int(nc) * _ES.get(t, 0) for nr, nc in zip(rows, cols)] * max(N, 0)
+    part = _shard_bytes(rows, cols, N, _ES.get(t, 0)) if N > 0 else []
+    like = None if isinstance(pa, ctypes.Array) else _first(pa)
+    _check(_c_fsdp2_ag(_bufs(sh, N * P, part, "shards"), _bufs(pa, N * P, full, "params"), _sz_array(rows),
+                       _sz_array(cols), P, N, t, _stream(stream, like)), "gc_fsdp2_all_gather")
     return params
 
 
@@ -328,31 +380,44 @@ def gc_moe_route_scratch_bytes(ntokens, topk, experts_per_rank):
     return int(_c_moe_scratch(_i64_array(ntokens), len(ntokens), int(topk), int(experts_per_rank)))
 
 
+def _per_route(ntokens, topk, nbytes):
+    return [max(0, int(t)) * max(0, int(topk)) * nbytes for t in ntokens]
+
+
 def gc_moe_route(experts, ntokens, topk, experts_per_rank, splits, dest, scratch, scratch_bytes=None, stream=None):
     """MoE routing plan on the device.  experts[s]: int32 [ntokens[s] * topk] global expert ids;
     splits: int64 [N*N*E] out; dest[s]: int32 [ntokens[s] * topk * 2] (rank, row) out."""
     n = len(ntokens)
     if scratch_bytes is None:
         scratch_bytes = scratch.numel() * scratch.element_size()
-    _check(_c_moe_route(_ptr_array(experts), _i64_array(ntokens), n, int(topk), int(experts_per_rank),
-                        _addr(splits), _ptr_array(dest), _addr(scratch), int(scratch_bytes),
-                        _stream(stream, splits)), "gc_moe_route")
+    nsplit = n * n * max(0, int(experts_per_rank)) * 8
+    _check(_c_moe_route(_bufs(experts, n, _per_route(ntokens, topk, 4), "experts"), _i64_array(ntokens), n,
+                        int(topk), int(experts_per_rank), _buf(splits, nsplit, "splits"),
+                        _bufs(dest, n, _per_route(ntokens, topk, 8), "dest"),
+                        _buf(scratch, int(scratch_bytes), "scratch"), int(scratch_bytes), _stream(stream, splits)),
+           "gc_moe_route")
     return splits, dest
 
 
 def gc_moe_dispatch(tokens, ntokens, dest, topk, row_bytes, recv, recv_rows, stream=None):
     """Copy every token row of every source to the receive rows its routes name."""
-    _check(_c_moe_dispatch(_ptr_array(tokens), _i64_array(ntokens), _ptr_array(dest), len(ntokens), int(topk),
-                           int(row_bytes), _ptr_array(recv), _i64_array(recv_rows),
+    n, rb = len(ntokens), int(row_bytes)
+    _check(_c_moe_dispatch(_bufs(tokens, n, [max(0, int(t)) * rb for t in ntokens], "tokens"), _i64_array(ntokens),
+                           _bufs(dest, n, _per_route(ntokens, topk, 8), "dest"), n, int(topk), rb,
+                           _bufs(recv, n, [max(0, int(r)) * rb for r in recv_rows], "recv"), _i64_array(recv_rows),
                            _stream(stream, _first(recv))), "gc_moe_dispatch")
     return recv
 
 
 def gc_moe_combine(expert_out, expert_rows, dest, weights, ntokens, topk, hidden, dtype, out, stream=None):
     """out[s][t] = sum_k weights[s][t*topk + k] * expert_out[rank][row] over the routes of token t."""
-    _check(_c_moe_combine(_ptr_array(expert_out), _i64_array(expert_rows), _ptr_array(dest), _ptr_array(weights),
-                          _i64_array(ntokens), len(ntokens), int(topk), int(hidden), _dtype_code(dtype),
-                          _ptr_array(out), _stream(stream, _first(out))), "gc_moe_combine")
+    n, t = len(ntokens), _dtype_code(dtype)
+    rb = max(0, int(hidden)) * _ES.get(t, 0)
+    _check(_c_moe_combine(_bufs(expert_out, n, [max(0, int(r)) * rb for r in expert_rows], "expert_out"),
+                          _i64_array(expert_rows), _bufs(dest, n, _per_route(ntokens, topk, 8), "dest"),
+                          _bufs(weights, n, _per_route(ntokens, topk, 4), "weights"), _i64_array(ntokens), n,
+                          int(topk), int(hidden), t, _bufs(out, n, [max(0, int(x)) * rb for x in ntokens], "out"),
+                          _stream(stream, _first(out))), "gc_moe_combine")
     return out
 
 
@@ -457,29 +522,34 @@ def gc_bucket_plan_destroy(plan):
 
 
 def gc_bucket_pack(plan, bucket, tensors, bucket_bufs, nranks, stream=None):
-    """tensors: flat rank-major list of nranks*ntensors tensors (or None for tensors outside the bucket)."""
-    _check(_c_pack(plan, int(bucket), _ptr_array(tensors), _ptr_array(bucket_bufs), int(nranks),
-                   _stream(stream, _first(bucket_bufs))), "gc_bucket_pack")
+    """tensors: flat rank-major list of nranks*ntensors tensors (or None for tensors outside the bucket).
+    The plan handle does not carry the tensor sizes, so only device and layout are checked here
+    (BucketPlan.pack checks sizes too)."""
+    _check(_c_pack(plan, int(bucket), _bufs(tensors, 0, 0, "tensors"), _bufs(bucket_bufs, 0, 0, "bucket_bufs"),
+                   int(nranks), _stream(stream, _first(bucket_bufs))), "gc_bucket_pack")
 
 
 def gc_bucket_unpack(plan, bucket, bucket_bufs, tensors, nranks, stream=None):
-    _check(_c_unpack(plan, int(bucket), _ptr_array(bucket_bufs), _ptr_array(tensors), int(nranks),
-                     _stream(stream, _first(bucket_bufs))), "gc_bucket_unpack")
+    _check(_c_unpack(plan, int(bucket), _bufs(bucket_bufs, 0, 0, "bucket_bufs"), _bufs(tensors, 0, 0, "tensors"),
+                     int(nranks), _stream(stream, _first(bucket_bufs))), "gc_bucket_unpack")
 
 
 def gc_bucket_all_reduce(plan, bucket, tensors, nranks, op="avg", order="ring", sumsq=None, stream=None):
     """Zero-copy all-reduce of one bucket, in place over the tensors (rank-major flat list).
     sumsq: optional CUDA float64 tensor (one element) that receives += sum of squared results."""
-    _check(_c_bucket_ar(plan, int(bucket), _ptr_array(tensors), int(nranks), _enum(_OP, op), _enum(_ORDER, order),
-                        _addr(sumsq), _stream(stream, _first(tensors))),
+    _check(_c_bucket_ar(plan, int(bucket), _bufs(tensors, 0, 0, "tensors"), int(nranks), _enum(_OP, op),
+                        _enum(_ORDER, order), _buf(sumsq, 8, "sumsq"), _stream(stream, _first(tensors))),
            "gc_bucket_all_reduce")
 
 
 class BucketPlan:
-    """Owns a gc_bucket_plan handle and caches its query results."""
+    """Owns a gc_bucket_plan handle and caches its query results.  Its calls
+    check every tensor and bucket buffer against the plan's sizes before the
+    library sees the pointers."""
 
     def __init__(self, numels, dtype, cap_bytes, reverse=True, pad_to=1):
         self.numels = [int(x) for x in numels]
+        self.es = _ES.get(_dtype_code(dtype), 0)
         self.handle = gc_bucket_plan_create(self.numels, dtype, cap_bytes, reverse, pad_to)
         self.nbuckets, self.bucket_numel, self.tensor_bucket, self.tensor_offset = gc_bucket_plan_query(
             self.handle, len(self.numels))
@@ -489,14 +559,31 @@ class BucketPlan:
         ts = [t for t in range(len(self.numels)) if self.tensor_bucket[t] == b]
         return sorted(ts, key=lambda t: self.tensor_offset[t])
 
+    def _tensors(self, bucket, tensors, nranks):
+        """Checked pointer array of the rank-major tensor list: bucket members need their full size."""
+        if isinstance(tensors, ctypes.Array):        # marshalled once by gc_pointers: only its length is checked
+            return _bufs(tensors, max(0, nranks) * len(self.numels), 0, "tensors")
+        need = [n * self.es if self.tensor_bucket[t] == bucket else 0 for t, n in enumerate(self.numels)]
+        return _bufs(tensors, max(0, nranks) * len(need), need * max(0, nranks), "tensors")
+
+    def _bucket_bufs(self, bucket, bufs, nranks):
+        nb = self.bucket_numel[bucket] * self.es if 0 <= bucket < self.nbuckets else 0
+        return _bufs(bufs, max(0, nranks), nb, "bucket_bufs")
+
     def pack(self, bucket, tensors, bucket_bufs, nranks, stream=None):
-        gc_bucket_pack(self.handle, bucket, tensors, bucket_bufs, nranks, stream)
+        stream = _stream(stream, _first(bucket_bufs))
+        gc_bucket_pack(self.handle, bucket, self._tensors(bucket, tensors, nranks),
+                       self._bucket_bufs(bucket, bucket_bufs, nranks), nranks, stream)
 
     def unpack(self, bucket, bucket_bufs, tensors, nranks, stream=None):
-        gc_bucket_unpack(self.handle, bucket, bucket_bufs, tensors, nranks, stream)
+        stream = _stream(stream, _first(bucket_bufs))
+        gc_bucket_unpack(self.handle, bucket, self._bucket_bufs(bucket, bucket_bufs, nranks),
+                         self._tensors(bucket, tensors, nranks), nranks, stream)
 
     def all_reduce(self, bucket, tensors, nranks, op="avg", order="ring", sumsq=None, stream=None):
-        gc_bucket_all_reduce(self.handle, bucket, tensors, nranks, op, order, sumsq, stream)
+        stream = _stream(stream, _first(tensors))
+        gc_bucket_all_reduce(self.handle, bucket, self._tensors(bucket, tensors, nranks), nranks, op, order, sumsq,
+                             stream)
 
     def close(self):
         if self.handle:

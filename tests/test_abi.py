@@ -323,3 +323,102 @@ def test_hier_and_hsdp_validation():
     bad = r[:5] + [s[5] + 2 * 10 * 2] + r[6:]                                                   # member 2's chunk
     assert _status(hrs, s, bad, 4, **dict(kw, out_dtype="bf16")) == gc.GC_ERR_INVALID_ARG
     assert _status(hrs, s, r, 4, **dict(kw, recv_count=0)) == gc.GC_OK
+
+
+class _DevTensor:
+    """Stands in for a device tensor in the binding's checks: an address, a size
+    and a layout flag.  Never dereferenced: every call below is stopped by the
+    binding or by the library's host-side validation."""
+
+    is_cuda = True
+
+    def __init__(self, addr, nbytes, contiguous=True):
+        self._addr, self._n, self._c = addr, nbytes, contiguous
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        return self._addr
+
+
+def test_binding_rejects_short_strided_and_host_tensors():
+    import torch
+    T = _DevTensor
+    send = [T(FAKE + i * (1 << 30), 64) for i in range(4)]
+    recv = [T(FAKE + (1 << 40) + i * (1 << 30), 64) for i in range(4)]
+    with pytest.raises(ValueError, match="buffers, the call needs 4"):      # recv list shorter than send
+        gc.gc_all_reduce(send, recv[:3], count=16, dtype="fp32", stream=0)
+    with pytest.raises(ValueError, match=r"recv\[2\]: 60 bytes"):           # one output too small
+        gc.gc_all_reduce(send, recv[:2] + [T(recv[2].data_ptr(), 60)] + recv[3:], count=16, dtype="fp32", stream=0)
+    with pytest.raises(ValueError, match="not contiguous"):
+        gc.gc_all_reduce([T(FAKE, 64, contiguous=False)] + send[1:], recv, count=16, dtype="fp32", stream=0)
+    with pytest.raises(ValueError, match="device"):                          # a host tensor
+        gc.gc_all_reduce([torch.zeros(16)] + send[1:], recv, count=16, dtype="fp32", stream=0)
+    # right sizes pass the binding; the library then rejects the partial overlap on the host
+    bad = recv[:3] + [T(send[0].data_ptr() + 4, 64)]
+    assert _status(gc.gc_all_reduce, send, bad, count=16, dtype="fp32", stream=0) == gc.GC_ERR_INVALID_ARG
+    # reduce-scatter: send holds N * recv_count elements, recv recv_count of the output type
+    with pytest.raises(ValueError, match=r"send\[0\]: 64 bytes, the call touches 72"):
+        gc.gc_reduce_scatter(send, recv, recv_count=9, in_dtype="bf16", out_dtype="fp32", stream=0)
+    with pytest.raises(ValueError, match=r"recv\[0\]"):
+        gc.gc_all_gather(send, [T(FAKE + (1 << 40), 255)] + recv[1:], count=16, dtype="fp32", stream=0)
+    # all-to-all: send[s] needs its rows to every destination, recv[d] the rows from every source
+    sp = [[[1], [2]], [[3], [4]]]
+    big = [T(FAKE + i * (1 << 30), 256) for i in range(2)]
+    with pytest.raises(ValueError, match=r"recv\[1\]: 64 bytes"):           # 2 + 4 rows of 16 B
+        gc.gc_all_to_all(big, recv[:2], sp, 16, stream=0)
+    with pytest.raises(ValueError, match=r"send\[1\]: 64 bytes"):           # 3 + 4 rows of 16 B
+        gc.gc_all_to_all(send[:2], big, sp, 16, stream=0)
+    # MoE combine: out[s] holds ntokens[s] rows of hidden elements
+    with pytest.raises(ValueError, match=r"out\[0\]"):
+        gc.gc_moe_combine(recv[:2], [2, 2], send[:2], send[2:], [3, 0], 2, 16, "bf16", recv[2:], stream=0)
+    with pytest.raises(ValueError, match="the call needs 2"):
+        gc.gc_moe_dispatch(send[:2], [1, 1], send[2:3], 2, 16, recv[:2], [1, 1], stream=0)
+
+
+def test_bucket_plan_checks_sizes_against_the_plan():
+    T = _DevTensor
+    plan = gc.BucketPlan([8, 8, 100], "bf16", 32, reverse=False)   # buckets [0, 1] and [2]
+    try:
+        assert plan.nbuckets == 2
+        tensors = [T(FAKE + i * (1 << 30), n * 2) for i, n in enumerate([8, 8, 100] * 2)]
+        bufs = [T(FAKE + (1 << 40) + r * (1 << 30), 32) for r in range(2)]
+        short = list(tensors)
+        short[4] = T(tensors[4].data_ptr(), 15)                    # rank 1, tensor 1: 16 B needed
+        with pytest.raises(ValueError, match=r"tensors\[4\]: 15 bytes"):
+            plan.pack(0, short, bufs, 2, stream=0)
+        with pytest.raises(ValueError, match=r"tensors\[4\]"):
+            plan.all_reduce(0, short, 2, stream=0)
+        short[4] = None                                            # outside bucket 1: not checked
+        with pytest.raises(ValueError, match=r"bucket_bufs\[0\]: 32 bytes"):
+            plan.unpack(1, bufs, short, 2, stream=0)               # bucket 1 holds 100 bf16
+        with pytest.raises(ValueError, match="the call needs 6"):
+            plan.all_reduce(0, tensors[:5], 2, stream=0)
+        with pytest.raises(ValueError, match="sumsq: 4 bytes"):
+            plan.all_reduce(0, tensors, 2, sumsq=T(FAKE + (1 << 42), 4), stream=0)
+    finally:
+        plan.close()
+
+
+def test_fsdp2_binding_checks_shard_sizes():
+    T = _DevTensor
+    N, rows, cols = 4, [3, 2], [5, 2]                   # shards of rows: [1,1,1,0] and [1,1,0,0]
+    G_ = [[T(FAKE + (r * 2 + p) * (1 << 30), rows[p] * cols[p] * 2) for p in range(2)] for r in range(N)]
+    S_ = [[T(FAKE + (1 << 40) + (r * 2 + p) * (1 << 30), 64) for p in range(2)] for r in range(N)]
+    S_[2][1] = S_[3][1] = 0                              # empty shards may be NULL
+    S_[1][0] = T(S_[1][0].data_ptr(), 5 * 4 - 1)         # one row of 5 fp32 needs 20 B
+    with pytest.raises(ValueError, match=r"shards\[2\]: 19 bytes"):
+        gc.gc_fsdp2_reduce_scatter(G_, S_, rows, cols, N, "bf16", "fp32", stream=0)
+    S_[1][0] = T(S_[1][0].data_ptr(), 20)
+    P_ = [[T(FAKE + (1 << 41) + (r * 2 + p) * (1 << 30), rows[p] * cols[p] * 2) for p in range(2)]
+          for r in range(N)]
+    P_[3][0] = T(P_[3][0].data_ptr(), 29)                # 3 x 5 bf16 = 30 B
+    with pytest.raises(ValueError, match=r"params\[6\]: 29 bytes"):
+        gc.gc_fsdp2_all_gather(S_, P_, rows, cols, N, "bf16", stream=0)
