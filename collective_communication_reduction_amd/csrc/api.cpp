@@ -58,6 +58,26 @@ gc_status check_ptrs(const void* const* p, int n, size_t es) {
   return GC_OK;
 }
 
+// Store policy of each use of the segment copy (measured on MI355X in one
+// process on the same buffers).  Device-scope stores speed up these one-stream
+// copies: the 8-rank MoE all-to-all went from 677 to 653 us (659 without the
+// non-temporal hint).  The pack leaves out the hint so that the bucket can stay
+// in the MALL for the all-reduce that reads it next: the 226-bucket DDP step
+// went from 102.4 to 95.6 ms (99.4 with the hint; the unpack's choice moved it
+// by 0.3 %).
+#ifndef GC_A2A_STORE
+#define GC_A2A_STORE gci::kStoreDevNT
+#endif
+#ifndef GC_PACK_STORE
+#define GC_PACK_STORE gci::kStoreDev
+#endif
+#ifndef GC_UNPACK_STORE
+#define GC_UNPACK_STORE gci::kStoreDevNT
+#endif
+constexpr gci::StorePolicy kA2aStore = GC_A2A_STORE;
+constexpr gci::StorePolicy kPackStore = GC_PACK_STORE;
+constexpr gci::StorePolicy kUnpackStore = GC_UNPACK_STORE;
+
 #define GC_TRY(expr)                    \
   do {                                  \
     const gc_status _s = (expr);        \
@@ -289,7 +309,7 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
         run += v;
       }
   }
-  return gci::launch_segment_copy(segs.data(), segs.size(), stream);
+  return gci::launch_segment_copy(segs.data(), segs.size(), kA2aStore, stream);
 }
 
 // ------------------------------------------------------- two-level / HSDP
@@ -804,7 +824,7 @@ extern "C" gc_status gc_bucket_pack(const gc_bucket_plan* p, int bucket, const v
   if (!tensors || !bucket_bufs) return GC_ERR_INVALID_ARG;
   std::vector<gci::Segment> segs;
   GC_TRY(bucket_segments(p, bucket, tensors, nullptr, nullptr, bucket_bufs, nranks, true, &segs));
-  return gci::launch_segment_copy(segs.data(), segs.size(), stream);
+  return gci::launch_segment_copy(segs.data(), segs.size(), kPackStore, stream);
 }
 
 extern "C" gc_status gc_bucket_unpack(const gc_bucket_plan* p, int bucket, const void* const* bucket_bufs,
@@ -812,5 +832,5 @@ extern "C" gc_status gc_bucket_unpack(const gc_bucket_plan* p, int bucket, const
   if (!tensors || !bucket_bufs) return GC_ERR_INVALID_ARG;
   std::vector<gci::Segment> segs;
   GC_TRY(bucket_segments(p, bucket, nullptr, tensors, bucket_bufs, nullptr, nranks, false, &segs));
-  return gci::launch_segment_copy(segs.data(), segs.size(), stream);
+  return gci::launch_segment_copy(segs.data(), segs.size(), kUnpackStore, stream);
 }

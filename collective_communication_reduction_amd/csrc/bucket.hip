@@ -28,6 +28,12 @@ namespace {
 
 using namespace gcdev;
 
+// Cache policy of the in-place results' 16-byte stores: device scope measured
+// 34.55 against 34.77 ms for the 226 buckets of the 8-rank DDP step.
+#ifndef GC_BUCKET_STORE
+#define GC_BUCKET_STORE gci::kStoreDevNT
+#endif
+
 constexpr int kMaxPieces = 40;
 
 struct PieceDev {
@@ -110,7 +116,7 @@ __device__ __forceinline__ double bucket_tile(const BucketArgs<P, MAXS>& a, cons
     for (int l = 0; l < VE; ++l) o[l] = finish(acc[u][l], avg, a.nf);
     const Words<Out, VE> w = pack<Out, VE>(o);
     if (!GUARD || v < nvec) {
-      for (uint32_t q = 0; q < N; ++q) put<Out, VE>(a.ptr[pc.slot][q] + off[u], w);
+      for (uint32_t q = 0; q < N; ++q) put<Out, VE, GC_BUCKET_STORE>(a.ptr[pc.slot][q] + off[u], w);
       if constexpr (SUMSQ) {
 #pragma unroll
         for (int l = 0; l < VE; ++l) {

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gc_internal.h"
+
 namespace gcdev {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -46,6 +48,22 @@ __device__ __forceinline__ void st8(void* p, u32x2 v) {
 #else
   *reinterpret_cast<u32x2*>(p) = v;
 #endif
+}
+
+// 16-byte store with a cache policy (gci::StorePolicy).  Device scope has no
+// builtin for a 16-byte store, so those two are inline assembly.  A VALU write
+// to the data registers of a store wider than 8 bytes needs two wait states
+// after the store on this architecture; the compiler inserts them after its own
+// stores but cannot after an asm statement, hence the s_nop (two wait states).
+template <int POL>
+__device__ __forceinline__ void st16p(void* p, u32x4 v) {
+  if constexpr (POL == gci::kStoreDevNT) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
+  } else if constexpr (POL == gci::kStoreDev) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
+  } else {
+    st16(p, v);
+  }
 }
 
 // ---------------------------------------------------------------- inputs

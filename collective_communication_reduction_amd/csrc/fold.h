@@ -53,14 +53,15 @@ __device__ __forceinline__ Words<Out, VE> pack(const Acc (&x)[VE]) {
   return r;
 }
 
-template <class Out, int VE>
+template <class Out, int VE, int POL = gci::kStoreNT>
 __device__ __forceinline__ void put(char* p, const Words<Out, VE>& r) {
   constexpr int NW = Words<Out, VE>::NW;
   if constexpr (NW == 2) {
     st8(p, u32x2{r.w[0], r.w[1]});
   } else {
 #pragma unroll
-    for (int h = 0; h < NW / 4; ++h) st16(p + 16 * h, u32x4{r.w[4 * h], r.w[4 * h + 1], r.w[4 * h + 2], r.w[4 * h + 3]});
+    for (int h = 0; h < NW / 4; ++h)
+      st16p<POL>(p + 16 * h, u32x4{r.w[4 * h], r.w[4 * h + 1], r.w[4 * h + 2], r.w[4 * h + 3]});
   }
 }
 

@@ -85,6 +85,13 @@ struct BucketCall {
 
 gc_status launch_bucket_all_reduce(const BucketCall& call);
 
+// Cache policy of a kernel's 16-byte stores.  kStoreNT: the non-temporal hint
+// alone.  kStoreDevNT: device scope (sc1) plus the hint: the line is written
+// through the XCD's L2 rather than left there dirty.  kStoreDev: device scope
+// without the hint, so the line may stay in the MALL for the kernel that reads
+// it next.
+enum StorePolicy : int { kStoreNT = 0, kStoreDevNT = 1, kStoreDev = 2 };
+
 // One contiguous copy; src == nullptr writes zeros.
 struct Segment {
   const void* src;
@@ -92,7 +99,7 @@ struct Segment {
   uint64_t bytes;
 };
 
-gc_status launch_segment_copy(const Segment* segs, size_t nseg, hipStream_t stream);
+gc_status launch_segment_copy(const Segment* segs, size_t nseg, StorePolicy pol, hipStream_t stream);
 
 
 // MoE routing plan (see gc_moe_route).  Routes of source s are cut into tiles

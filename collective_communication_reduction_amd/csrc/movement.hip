@@ -98,6 +98,8 @@ __device__ __forceinline__ SegDesc find_segment(const SegArgs& a, const SegLooku
 
 // Segments whose source and destination agree modulo 16 bytes: byte head up
 // to the first 16-byte boundary of the destination, 16-byte body, byte tail.
+// POL is the body stores' cache policy (gci::StorePolicy).
+template <int POL>
 __global__ void __launch_bounds__(kThreads) segment_vec_kernel(const SegArgs a) {
   const SegLookup l = seg_lookup(a);
   // The grid never exceeds the tile count, so every workgroup has a first tile
@@ -124,7 +126,7 @@ __global__ void __launch_bounds__(kThreads) segment_vec_kernel(const SegArgs a) 
 #pragma unroll
       for (int u = 0; u < kSegU; ++u) {
         const uint64_t v = v0 + u * kThreads;
-        if (v < nvec) st16(dst + head + 16 * v, buf[u]);
+        if (v < nvec) st16p<POL>(dst + head + 16 * v, buf[u]);
       }
     }
     if (t == 0) {
@@ -197,7 +199,7 @@ int narrow_width(const gci::Segment& s) {
 bool vec_ok(const gci::Segment& s) { return !s.src || ((addr(s.src) ^ addr(s.dst)) & 15) == 0; }
 
 // Launch one batch of segments of one class (width 16 = vector kernel).
-gc_status launch_batch(const gci::Segment* segs, int n, int width, hipStream_t stream) {
+gc_status launch_batch(const gci::Segment* segs, int n, int width, gci::StorePolicy pol, hipStream_t stream) {
   SegArgs a{};
   std::fill(a.tile0, a.tile0 + kMaxSeg, UINT32_MAX);
   std::fill(a.coarse, a.coarse + kSegGroups, UINT32_MAX);
@@ -220,7 +222,12 @@ gc_status launch_batch(const gci::Segment* segs, int n, int width, hipStream_t s
   a.nseg = static_cast<uint32_t>(n);
   const uint32_t grid = std::min(tiles, kMaxGrid);
   switch (width) {
-    case 16: return launch(segment_vec_kernel, a, grid, stream);
+    case 16:
+      switch (pol) {
+        case gci::kStoreDevNT: return launch(segment_vec_kernel<gci::kStoreDevNT>, a, grid, stream);
+        case gci::kStoreDev: return launch(segment_vec_kernel<gci::kStoreDev>, a, grid, stream);
+        default: return launch(segment_vec_kernel<gci::kStoreNT>, a, grid, stream);
+      }
     case 8: return launch(segment_narrow_kernel<uint64_t>, a, grid, stream);
     case 4: return launch(segment_narrow_kernel<uint32_t>, a, grid, stream);
     case 2: return launch(segment_narrow_kernel<uint16_t>, a, grid, stream);
@@ -232,7 +239,7 @@ gc_status launch_batch(const gci::Segment* segs, int n, int width, hipStream_t s
 
 namespace gci {
 
-gc_status launch_segment_copy(const Segment* segs, size_t nseg, hipStream_t stream) {
+gc_status launch_segment_copy(const Segment* segs, size_t nseg, StorePolicy pol, hipStream_t stream) {
   // Group by copy class, then launch in batches of at most kMaxSeg.
   for (int width : {16, 8, 4, 2, 1}) {
     Segment batch[kMaxSeg];
@@ -244,13 +251,13 @@ gc_status launch_segment_copy(const Segment* segs, size_t nseg, hipStream_t stre
       if (w != width) continue;
       batch[n++] = s;
       if (n == kMaxSeg) {
-        const gc_status st = launch_batch(batch, n, width, stream);
+        const gc_status st = launch_batch(batch, n, width, pol, stream);
         if (st != GC_OK) return st;
         n = 0;
       }
     }
     if (n) {
-      const gc_status st = launch_batch(batch, n, width, stream);
+      const gc_status st = launch_batch(batch, n, width, pol, stream);
       if (st != GC_OK) return st;
     }
   }
