@@ -923,7 +923,7 @@ def main():
     if not args.no_copy_ceiling:
         ceiling = copy_ceiling()
         out["copy_ceiling"] = {"value": round(ceiling, 2), "unit": "GB/s",
-                               "kernel": "segment_vec_kernel, one 2 GiB block (16-byte loads and stores)",
+                               "kernel": "segment_vec_kernel, one 2 GiB block (16-byte loads, 16-byte device-scope stores)",
                                "frac": round(achieved / ceiling, 4)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.seed)
