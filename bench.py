@@ -321,7 +321,10 @@ class DdpWorkload(Workload):
     def config(self):
         return {"workload": self.name, "nranks": self.N, "params": sum(self.numels), "storage": "bf16",
                 "buckets": self.plan.nbuckets, "cap_bytes": 25 * 1024 * 1024, "op": "avg", "order": "ring",
-                "zero_copy": self.zero_copy, "layout": self.layout}
+                "zero_copy": self.zero_copy, "layout": self.layout,
+                **({} if self.zero_copy else {
+                    "cache_note": "each bucket is read by the all-reduce right after its pack, and part of it is "
+                                  "then served by the 256 MB MALL: value counts algorithmic bytes, not HBM bytes"})}
 
     def cpu_sample(self, seed):
         import numpy as np
