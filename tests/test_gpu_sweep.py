@@ -8,7 +8,10 @@ place.  Each case is drawn from its own seed, printed in the test id, so a
 failure names a case that reruns alone.
 
 Tolerance as in the parity tests: bit-exact for fp32, int32 and movement;
-bf16 within 1 ulp and expected bit-exact."""
+bf16 within 1 ulp and expected bit-exact.  Every view sits inside its own
+allocation filled with a sentinel: after the call nothing outside the views
+may have changed, and inputs (outside an in-place output) must still hold
+their values."""
 
 import numpy as np
 import pytest
@@ -52,8 +55,39 @@ def _offsets(rng, N):
     return [int(x) for x in rng.integers(0, 8, size=N)]
 
 
+GUARD = 64
+SENTINEL = {2: 0x7FC1, 4: 0x7FC00001}     # by element size: a NaN pattern no result here takes
+
+
+def _ints(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+
 def _views(n, dtype, offsets):
-    return [empty(n + 8, dtype)[o:o + n] for o in offsets]
+    """Views of n elements at the given element offsets, each inside its own
+    allocation filled with a sentinel (checked by _untouched)."""
+    out = []
+    for o in offsets:
+        full = empty(o + n + GUARD, dtype)
+        _ints(full).fill_(SENTINEL[full.element_size()])
+        out.append(full[o:o + n])
+    return out
+
+
+def _untouched(views, what):
+    """Every element of each view's allocation outside the view still holds the sentinel."""
+    for r, v in enumerate(views):
+        full = v._base
+        off = v.storage_offset() - full.storage_offset()
+        bits = _ints(full).cpu().numpy()
+        s = SENTINEL[v.element_size()]
+        assert np.all(bits[:off] == s) and np.all(bits[off + v.numel():] == s), f"{what}: rank {r} guard written"
+
+
+def _unchanged(views, values, dtype, what):
+    """Inputs are never written: each view still holds its values."""
+    for r, (v, x) in enumerate(zip(views, values)):
+        assert_same(from_dev(v), np.asarray(x), dtype, f"{what}: input {r} changed")
 
 
 def _check(got, want, dtype, what):
@@ -89,6 +123,10 @@ def test_all_reduce_sweep(seed):
     torch.cuda.synchronize()
     for r in _sample_ranks(N):
         _check(from_dev(recv[r]), want, dtype, f"{case} rank {r}")
+    _untouched(send, case)
+    if not in_place:
+        _untouched(recv, case)
+        _unchanged([send[r] for r in _sample_ranks(N)], [xs[r] for r in _sample_ranks(N)], dtype, case)
 
 
 @pytest.mark.parametrize("seed", range(48))
@@ -114,6 +152,17 @@ def test_reduce_scatter_sweep(seed):
     torch.cuda.synchronize()
     for j in _sample_ranks(N):
         _check(from_dev(recv[j]), want[j], tout, f"{case} owner {j}")
+    _untouched(send, case)
+    for r in _sample_ranks(N):
+        if in_place:        # the rest of the owner's send buffer is input and stays as it was
+            got, x = from_dev(send[r]), np.asarray(xs[r])
+            keep = np.ones(N * rc, dtype=bool)
+            keep[r * rc:(r + 1) * rc] = False
+            assert_same(got[keep], x[keep], tin, f"{case}: input {r} changed outside its shard")
+        else:
+            _unchanged([send[r]], [xs[r]], tin, case)
+    if not in_place:
+        _untouched(recv, case)
 
 
 @pytest.mark.parametrize("seed", range(32))
@@ -138,6 +187,10 @@ def test_all_gather_sweep(seed):
     torch.cuda.synchronize()
     for d in _sample_ranks(N):
         assert_same(from_dev(recv[d]), want[d], dtype, f"{case} rank {d}")
+    _untouched(recv, case)
+    if not in_place:
+        _untouched(send, case)
+        _unchanged([send[r] for r in _sample_ranks(N)], [shards[r] for r in _sample_ranks(N)], dtype, case)
 
 
 @pytest.mark.parametrize("seed", range(24))
@@ -161,6 +214,9 @@ def test_two_level_all_reduce_sweep(seed):
     torch.cuda.synchronize()
     for r in _sample_ranks(N):
         _check(from_dev(recv[r]), want, dtype, f"{case} rank {r}")
+    _untouched(send, case)
+    _untouched(recv, case)
+    _unchanged([send[r] for r in _sample_ranks(N)], [xs[r] for r in _sample_ranks(N)], dtype, case)
 
 
 @pytest.mark.parametrize("seed", range(24))
@@ -187,6 +243,18 @@ def test_hsdp_reduce_scatter_sweep(seed):
     torch.cuda.synchronize()
     for r in _sample_ranks(N):
         _check(from_dev(recv[r]), want[r], tout, f"{case} rank {r}")
+    _untouched(send, case)
+    for r in _sample_ranks(N):
+        if in_place:        # outside member i's chunk the send buffer is input and stays as it was
+            i = r % Sg
+            got, x = from_dev(send[r]), np.asarray(xs[r])
+            keep = np.ones(Sg * rc, dtype=bool)
+            keep[i * rc:(i + 1) * rc] = False
+            assert_same(got[keep], x[keep], tin, f"{case}: input {r} changed outside its shard")
+        else:
+            _unchanged([send[r]], [xs[r]], tin, case)
+    if not in_place:
+        _untouched(recv, case)
 
 
 @pytest.mark.parametrize("seed", range(24))
