@@ -193,11 +193,15 @@ def test_combine(dtype, hidden, K, drop):
     want = M.combine(y, experts, w, N, E, hidden, dtype)
     y_dev = [to_dev(a, dtype) for a in y]
     w_dev = [torch.from_numpy(ws.reshape(-1)).to(DEV) for ws in w]
-    out = [torch.full((max(1, t * hidden),), 7.0, dtype=y_dev[0].dtype, device=DEV) for t in T]
+    # each output is a view with 64 sentinel elements after it: nothing past a source's rows may be written
+    out_full = [torch.full((t * hidden + 64,), 7.0, dtype=y_dev[0].dtype, device=DEV) for t in T]
+    out = [o[:t * hidden] for o, t in zip(out_full, T)]
     gc.gc_moe_combine(y_dev, [int(r) for r in rows], dest, w_dev, ntok, K, hidden, dtype, out)
     torch.cuda.synchronize()
     for s in range(N):
-        assert_same(from_dev(out[s])[:T[s] * hidden], want[s], dtype, f"source {s}")
+        assert_same(from_dev(out[s]), want[s], dtype, f"source {s}")
+        tail = out_full[s][T[s] * hidden:]
+        assert torch.equal(tail, torch.full_like(tail, 7.0)), f"source {s}: written past its rows"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
