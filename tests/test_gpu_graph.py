@@ -139,3 +139,60 @@ def test_moe_route_dispatch_combine_replayed():
         for s in range(N):
             if T[s]:
                 assert_same(from_dev(out[s])[:T[s] * H], want[s], "bf16", f"replay {rep} source {s}")
+
+
+def test_bucket_pack_all_reduce_unpack_and_all_to_all_replayed():
+    """The segment copy in a graph: a DDP bucket step (pack with zero padding,
+    all-reduce of the bucket, unpack) and an all-to-all(v) with experts."""
+    N = 4
+    numels = [1000, 37, 4096, 8, 513, 0, 7]
+    plan = gc.BucketPlan(numels, "bf16", cap_bytes=6000, reverse=True, pad_to=N)
+    try:
+        T = len(numels)
+        tensors = [[empty(max(1, n), "bf16")[:n] for n in numels] for _ in range(N)]
+        flat = [t for row in tensors for t in row]
+        bufs = [[empty(plan.bucket_numel[b], "bf16") for _ in range(N)] for b in range(plan.nbuckets)]
+        E, rb = 3, 48
+        rng = np.random.default_rng(5)
+        splits = rng.integers(0, 40, size=(N, N, E)).astype(np.int64)
+        send = [torch.empty(max(1, int(splits[s].sum()) * rb), dtype=torch.uint8, device=DEV) for s in range(N)]
+        rrows = splits.sum(axis=(0, 2))
+        recv = [torch.empty(max(1, int(rrows[d]) * rb), dtype=torch.uint8, device=DEV) for d in range(N)]
+
+        def step():
+            for b in range(plan.nbuckets):
+                plan.pack(b, flat, bufs[b], N)
+                gc.gc_all_reduce(bufs[b], bufs[b], op="avg", order="ring")
+                plan.unpack(b, bufs[b], flat, N)
+            gc.gc_all_to_all(send, recv, splits, rb)
+        for r in range(N):
+            for t in tensors[r]:
+                t.zero_()
+        g = _capture(step)
+        for rep in range(3):
+            host = [[G.normal_bf16(G.stream_key(300 + rep, r, t), np.arange(n), 1e-2) for t, n in enumerate(numels)]
+                    for r in range(N)]
+            for r in range(N):
+                for t, n in enumerate(numels):
+                    if n:
+                        tensors[r][t].copy_(to_dev(host[r][t], "bf16"))
+            sends = [rng.integers(0, 256, size=int(splits[s].sum()) * rb, dtype=np.uint8) for s in range(N)]
+            for s in range(N):
+                if sends[s].size:
+                    send[s][:sends[s].size].copy_(torch.from_numpy(sends[s]).to(DEV))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for b in range(plan.nbuckets):
+                ts = plan.bucket_tensors(b)
+                want = OB.bucket_all_reduce(host, ts, numels, "bf16", "avg", "ring", pad_to=N)
+                for t in ts:
+                    if numels[t]:
+                        for r in (0, N - 1):
+                            assert_same(from_dev(tensors[r][t]), want[r][t], "bf16", f"replay {rep} tensor {t}")
+            want_a2a = C.all_to_all(sends, splits, rb)
+            for d in range(N):
+                got = recv[d].cpu().numpy()[:len(want_a2a[d])]
+                assert np.array_equal(got, want_a2a[d]), f"replay {rep} all-to-all rank {d}"
+    finally:
+        plan.close()
