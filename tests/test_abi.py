@@ -422,3 +422,21 @@ def test_fsdp2_binding_checks_shard_sizes():
     P_[3][0] = T(P_[3][0].data_ptr(), 29)                # 3 x 5 bf16 = 30 B
     with pytest.raises(ValueError, match=r"params\[6\]: 29 bytes"):
         gc.gc_fsdp2_all_gather(S_, P_, rows, cols, N, "bf16", stream=0)
+
+
+def test_binding_shard_extents_follow_the_shard_rule():
+    """The binding sizes its FSDP2 checks with the dim-0 shard rule; it must
+    agree with the oracle's (torch.chunk) rule for every shape, or a short
+    shard could pass the check."""
+    import random
+    rng = random.Random(3)
+    for _ in range(300):
+        N = rng.randint(1, 64)
+        P = rng.randint(1, 6)
+        rows = [rng.choice([0, 1, rng.randint(0, 3 * N), rng.randint(0, 5000)]) for _ in range(P)]
+        cols = [rng.randint(0, 9) for _ in range(P)]
+        es = rng.choice([2, 4])
+        got = gc._shard_bytes(rows, cols, N, es)
+        want = [(hi - lo) * cols[p] * es for r in range(N)
+                for p in range(P) for lo, hi in [OB.uneven_dim0_shards(rows[p], N)[r]]]
+        assert got == want, (N, rows, cols)
