@@ -549,15 +549,17 @@ class BucketPlan:
 
     def __init__(self, numels, dtype, cap_bytes, reverse=True, pad_to=1):
         self.numels = [int(x) for x in numels]
+        self.reverse = bool(reverse)
         self.es = _ES.get(_dtype_code(dtype), 0)
         self.handle = gc_bucket_plan_create(self.numels, dtype, cap_bytes, reverse, pad_to)
         self.nbuckets, self.bucket_numel, self.tensor_bucket, self.tensor_offset = gc_bucket_plan_query(
             self.handle, len(self.numels))
 
     def bucket_tensors(self, b):
-        """Tensor indices of bucket b in packing order."""
+        """Tensor indices of bucket b in packing order (an empty tensor shares its
+        offset with the next one, so ties follow the visiting order)."""
         ts = [t for t in range(len(self.numels)) if self.tensor_bucket[t] == b]
-        return sorted(ts, key=lambda t: self.tensor_offset[t])
+        return sorted(ts, key=lambda t: (self.tensor_offset[t], -t if self.reverse else t))
 
     def _tensors(self, bucket, tensors, nranks):
         """Checked pointer array of the rank-major tensor list: bucket members need their full size."""

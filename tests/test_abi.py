@@ -440,3 +440,18 @@ def test_binding_shard_extents_follow_the_shard_rule():
         want = [(hi - lo) * cols[p] * es for r in range(N)
                 for p in range(P) for lo, hi in [OB.uneven_dim0_shards(rows[p], N)[r]]]
         assert got == want, (N, rows, cols)
+
+
+@pytest.mark.parametrize("reverse", [True, False])
+def test_bucket_tensors_keep_the_visiting_order_with_empty_tensors(reverse):
+    import random
+    rng = random.Random(7 if reverse else 8)
+    for _ in range(50):
+        numels = [rng.choice([0, 0, 1, rng.randint(0, 5000)]) for _ in range(rng.randint(1, 25))]
+        cap = rng.randint(1, 20000)
+        plan = gc.BucketPlan(numels, "bf16", cap, reverse=reverse)
+        try:
+            got = [plan.bucket_tensors(b) for b in range(plan.nbuckets)]
+        finally:
+            plan.close()
+        assert got == OB.assign_buckets(numels, 2, cap, reverse=reverse), (numels, cap)
