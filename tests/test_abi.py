@@ -455,3 +455,21 @@ def test_bucket_tensors_keep_the_visiting_order_with_empty_tensors(reverse):
         finally:
             plan.close()
         assert got == OB.assign_buckets(numels, 2, cap, reverse=reverse), (numels, cap)
+
+
+def test_rank_arena_layout():
+    """Every rank owns one region; a buffer sits at the same offset of every
+    region (256-byte steps), regions are region + stagger bytes apart, and a
+    full region raises instead of spilling into the next rank's."""
+    import torch
+    arena = gc.RankArena(4, region_bytes=1 << 16, stagger_bytes=4096, device="cpu")
+    a = arena.alloc(1000, "bf16")                    # 2000 B -> next offset 2048
+    b = arena.alloc(10, "fp32")
+    base = arena.slab.data_ptr()
+    step = (1 << 16) + 4096
+    for r in range(4):
+        assert a[r].numel() == 1000 and a[r].dtype == torch.bfloat16 and a[r].is_contiguous()
+        assert a[r].data_ptr() - base == r * step
+        assert b[r].data_ptr() - base == r * step + 2048
+    with pytest.raises(MemoryError):
+        arena.alloc((1 << 16) // 4, "fp32")          # 64 KiB more does not fit the 62 KiB left
