@@ -476,8 +476,8 @@ extern "C" gc_status gc_fsdp2_reduce_scatter(const void* const* grads, void* con
     const uint64_t S = rows[p] * cols[p];
     if (S == 0) continue;
     for (int r = 0; r < N; ++r) {
-      in[r] = grads[r * P + p];
-      out[r] = shards[r * P + p];
+      in[r] = grads[static_cast<size_t>(r) * P + p];
+      out[r] = shards[static_cast<size_t>(r) * P + p];
     }
     const uint64_t c = (rows[p] + N - 1) / N * cols[p];
     gci::ReduceCall call{in.data(), out.data(), N, S, c, in_t, out_t, op == GC_AVG, order != GC_ORDER_RANK, stream};
@@ -502,8 +502,8 @@ extern "C" gc_status gc_fsdp2_all_gather(const void* const* shards, void* const*
     const uint64_t S = rows[p] * cols[p];
     if (S == 0) continue;
     for (int r = 0; r < N; ++r) {
-      in[r] = shards[r * P + p];
-      out[r] = params[r * P + p];
+      in[r] = shards[static_cast<size_t>(r) * P + p];
+      out[r] = params[static_cast<size_t>(r) * P + p];
     }
     const uint64_t c = (rows[p] + N - 1) / N * cols[p];
     gci::ReduceCall call{in.data(), out.data(), N, S, c, t, t, false, false, stream};
@@ -658,6 +658,11 @@ extern "C" gc_status gc_moe_combine(const void* const* expert_out, const int64_t
 
 // ---------------------------------------------------------------- bucket plan
 
+namespace {
+// Largest padding multiple a plan accepts (FlatParameter pads to the rank count).
+constexpr size_t kMaxPadTo = size_t(1) << 20;
+}  // namespace
+
 struct gc_bucket_plan {
   gc_dtype t;
   size_t es;
@@ -673,7 +678,8 @@ extern "C" gc_status gc_bucket_plan_create(const size_t* numels, int ntensors, g
                                            int reverse, size_t pad_to, gc_bucket_plan** out) {
   if (!out) return GC_ERR_INVALID_ARG;
   *out = nullptr;
-  if (ntensors < 0 || (ntensors > 0 && !numels) || !valid_dtype(t) || pad_to == 0) return GC_ERR_INVALID_ARG;
+  if (ntensors < 0 || (ntensors > 0 && !numels) || !valid_dtype(t) || pad_to == 0 || pad_to > kMaxPadTo)
+    return GC_ERR_INVALID_ARG;
   gc_bucket_plan* p = new (std::nothrow) gc_bucket_plan;
   if (!p) return GC_ERR_NO_MEMORY;
   try {
@@ -699,7 +705,10 @@ extern "C" gc_status gc_bucket_plan_create(const size_t* numels, int ntensors, g
     };
     for (int k = 0; k < ntensors; ++k) {
       const int ti = reverse ? ntensors - 1 - k : k;
-      if (mul_overflows(p->numel[ti], 4) || cur_elems + p->numel[ti] < cur_elems) {
+      // A bucket's bytes must stay representable: every size the plan hands out is
+      // elements * element size (and padded up to pad_to elements).
+      if (mul_overflows(p->numel[ti], 4) || cur_elems + p->numel[ti] < cur_elems ||
+          mul_overflows(cur_elems + p->numel[ti] + pad_to, 4)) {
         delete p;
         return GC_ERR_INVALID_ARG;
       }

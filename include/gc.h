@@ -293,7 +293,9 @@ gc_status gc_moe_combine(const void* const* expert_out, const int64_t* expert_ro
  *   bytes reach cap_bytes (cap_bytes == SIZE_MAX: one bucket holding all
  *   tensors).  Tensors are never split.  Inside a bucket tensors are
  *   concatenated in visiting order; each bucket's length is padded with zeros
- *   to a multiple of pad_to elements (1: no padding; nranks: FlatParameter).
+ *   to a multiple of pad_to elements (1: no padding; nranks: FlatParameter;
+ *   at most 2^20).  A bucket whose padded bytes would not fit in 64 bits is
+ *   rejected with GC_ERR_INVALID_ARG.
  *   The plan is an immutable host object and may be shared across streams.
  */
 typedef struct gc_bucket_plan gc_bucket_plan;

@@ -155,6 +155,13 @@ def test_bucket_pack_validation():
     assert _status(plan.unpack, 0, bufs, tensors, 0, stream=0) == gc.GC_ERR_INVALID_ARG
     with pytest.raises(gc.GcError):
         gc.gc_bucket_plan_create([1, 2], "bf16", 10, pad_to=0)
+    with pytest.raises(gc.GcError):
+        gc.gc_bucket_plan_create([1, 2], "bf16", 10, pad_to=(1 << 20) + 1)   # above the padding limit
+    # a bucket whose padded bytes do not fit in 64 bits is refused
+    with pytest.raises(gc.GcError):
+        gc.gc_bucket_plan_create([8, (1 << 62) - 16], "fp32", gc.SIZE_MAX, pad_to=1 << 20)
+    with pytest.raises(gc.GcError):
+        gc.gc_bucket_plan_create([1 << 62], "bf16", gc.SIZE_MAX)
 
 
 def test_rank_buffers_layout():
