@@ -63,6 +63,27 @@ def reduce_scatter_at(values, owner, out_pos, recv_count, in_dtype, out_dtype, o
     return reduce_positions(values, in_dtype, starts, op, out_dtype, wire)
 
 
+def reduce_scatter_owner(chunks, owner, in_dtype, out_dtype, op, order, wire=None):
+    """Owner j's whole reduce-scatter output from chunks[i] = rank i's chunk j (any length).
+
+    Every element of chunk j has the same fold order, so the chunk is folded as
+    whole vectors: ranks j+1, j+2, ..., N-1, 0, ..., j in ring order (DTLM §2
+    "Reduce-Scatter"), 0, 1, ..., N-1 in rank order, starting from the first
+    term; wire="bf16" rounds each forwarded partial to bf16 first (DTLM §11).
+    Then the owner's epilogue.  This is how the full-size checks stream one
+    owner at a time through memory the step-by-step emulation cannot hold.
+    """
+    N = len(chunks)
+    first = (owner + 1) % N if order != "rank" else 0
+    acc = _widen(chunks[first], in_dtype)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for t in range(1, N):
+            if wire == "bf16":
+                acc = bf16_to_f32(f32_to_bf16(acc))
+            acc = acc + _widen(chunks[(first + t) % N], in_dtype)
+    return _epilogue(acc, op, N, out_dtype)
+
+
 def a2a_source_rows(splits, d, recv_rows):
     """For rows of rank d's receive buffer, the (source rank, source row) they come from."""
     splits = np.asarray(splits, dtype=np.int64)
@@ -106,6 +127,32 @@ def hier_fold_starts(positions, count, S, R, order, chunk=None):
     c2 = np.maximum(1, -(-L // R))
     h = (positions - lo) // c2
     return (h + 1) % R, (i + 1) % S
+
+
+def hier_reduce_block(values, S, g0, m0, dtype, op, out_dtype, wire=None):
+    """hier_reduce_positions for a block of positions that share one fold start
+    (a cell: one chunk i and one of its cross-group pieces h), folded as whole
+    vectors: groups g0, g0+1, ... (mod R), inside each group members m0, m0+1,
+    ... (mod S).  values[r] = rank r's inputs over the block.  wire="bf16"
+    rounds every forwarded partial to bf16 at both levels (DTLM §11)."""
+    N = len(values)
+    R = N // S
+    total = None
+    with np.errstate(over="ignore", invalid="ignore"):
+        for q in range(R):
+            g = (g0 + q) % R
+            part = _widen(values[g * S + m0], dtype)
+            for t in range(1, S):
+                if wire == "bf16":
+                    part = bf16_to_f32(f32_to_bf16(part))
+                part = part + _widen(values[g * S + (m0 + t) % S], dtype)
+            if total is None:
+                total = part
+            else:
+                if wire == "bf16":
+                    total = bf16_to_f32(f32_to_bf16(total))
+                total = total + part
+    return _epilogue(total, op, N, out_dtype)
 
 
 def hier_reduce_positions(values, S, g0, m0, dtype, op, out_dtype):

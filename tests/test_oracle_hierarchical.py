@@ -101,3 +101,66 @@ def test_sampled_two_level_matches_emulation(R, S, count, order):
         g0, m0 = SM.hier_fold_starts(pos, count, S, R, order, chunk=rc)
         got = SM.hier_reduce_positions(np.stack([x[pos] for x in xs]), S, g0, m0, "bf16", "avg", "fp32")
         assert np.array_equal(got, np.concatenate([sh[i] for i in range(S)]))
+
+
+# ---------------------------------------------------------------- bf16 on the wire
+
+@pytest.mark.parametrize("N,count", [(4, 4 * 37 + 3), (8, 100), (3, 2)])
+def test_wire_one_trivial_level_is_the_flat_wire_ring(N, count):
+    rng = np.random.default_rng(7 * N + count)
+    xs = [f32_to_bf16(rng.normal(size=count).astype(np.float32)) for _ in range(N)]
+    flat = C.all_reduce(xs, "bf16", "avg", "ring_wire")
+    for S in (N, 1):                     # one group of N, or N groups of one
+        got = H.all_reduce(xs, S, "bf16", "avg", "ring_wire")
+        assert all(np.array_equal(g, f) for g, f in zip(got, flat)), S
+
+
+def test_wire_worked_example():
+    # R = S = 2, one element per rank, bf16 bits: ranks (0,0), (0,1), (1,0), (1,1) hold 0, 2^-8, 2^-8, 1.
+    # Group 1 folds from member 1: 1 + 2^-8 (fp32, exact).  Group 0: 2^-8 + 0 = 2^-8.
+    # Across groups the fold starts at group 1, whose partial goes on the wire as bf16:
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 and rounds to even, 1; group 0 adds 2^-8 -> 1 + 2^-8,
+    # whose bf16 output (sum) is again the tie -> 1.0.  With fp32 partials the sum is 1 + 2^-7 exactly.
+    # The flat wire ring over the four ranks folds 2^-8, 2^-8, 1, 0 and never rounds: 1 + 2^-7.
+    one, eps, zero = 0x3F80, 0x3B80, 0x0000
+    xs = [np.array([b], np.uint16) for b in (zero, eps, eps, one)]
+    assert int(H.all_reduce(xs, 2, "bf16", "sum", "ring_wire")[0][0]) == 0x3F80
+    assert int(H.all_reduce(xs, 2, "bf16", "sum", "ring")[0][0]) == 0x3F81
+    assert int(C.all_reduce(xs, "bf16", "sum", "ring_wire")[0][0]) == 0x3F81
+    # the HSDP shard (one element per member chunk: count 2, chunk 0 holds element 0) sees the same rounding
+    ys = [np.array([b, zero], np.uint16) for b in (zero, eps, eps, one)]
+    sh = H.hsdp_reduce_scatter(ys, 2, "bf16", "fp32", "sum", "ring_wire")
+    assert float(sh[0][0]) == 1.0 + 2.0 ** -8 and float(sh[2][0]) == 1.0 + 2.0 ** -8
+    assert float(H.hsdp_reduce_scatter(ys, 2, "bf16", "fp32", "sum", "ring")[0][0]) == 1.0 + 2.0 ** -7
+
+
+@pytest.mark.parametrize("R,S,count", [(2, 8, 130), (4, 3, 50)])
+def test_wire_changes_nothing_for_fp32_data(R, S, count):
+    rng = np.random.default_rng(R + S)
+    xs = [rng.normal(size=count).astype(np.float32) for _ in range(R * S)]
+    a = H.all_reduce(xs, S, "fp32", "sum", "ring_wire")[0]
+    b = H.all_reduce(xs, S, "fp32", "sum", "ring")[0]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("R,S,count", [(2, 8, 301), (4, 3, 50), (3, 4, 7), (2, 2, 1), (2, 8, 320)])
+@pytest.mark.parametrize("order", ["ring", "rank", "ring_wire"])
+def test_block_evaluator_matches_emulation(R, S, count, order):
+    # each cell (chunk i, cross-group piece h) folded as one block with its fold start
+    from oracle import sampled as SM
+    rng = np.random.default_rng(R * S + count)
+    xs = [f32_to_bf16(rng.normal(size=count).astype(np.float32)) for _ in range(R * S)]
+    full = H.all_reduce(xs, S, "bf16", "avg", order)[0]
+    wire = "bf16" if order == "ring_wire" else None
+    c1 = -(-count // S)
+    got = np.empty(count, np.uint16)
+    for i in range(S):
+        lo, hi = min(count, i * c1), min(count, (i + 1) * c1)
+        c2 = max(1, -(-(hi - lo) // R))
+        for h in range(R):
+            a, b = lo + min(hi - lo, h * c2), lo + min(hi - lo, (h + 1) * c2)
+            if a == b:
+                continue
+            g0, m0 = ((h + 1) % R, (i + 1) % S) if order != "rank" else (0, 0)
+            got[a:b] = SM.hier_reduce_block([x[a:b] for x in xs], S, g0, m0, "bf16", "avg", "bf16", wire)
+    assert np.array_equal(got, full)
