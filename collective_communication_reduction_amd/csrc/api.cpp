@@ -316,10 +316,9 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
 
 namespace {
 
-gc_status check_mesh(int nranks, int group_size, gc_order order, gc_dtype t) {
+gc_status check_mesh(int nranks, int group_size) {
   GC_TRY(check_ranks(nranks));
   if (group_size < 1 || nranks % group_size) return GC_ERR_INVALID_ARG;
-  if (order == GC_ORDER_RING_WIRE && t == GC_BF16) return GC_ERR_UNSUPPORTED;
   return GC_OK;
 }
 
@@ -328,7 +327,7 @@ gc_status check_mesh(int nranks, int group_size, gc_order order, gc_dtype t) {
 extern "C" gc_status gc_hier_all_reduce(const void* const* send, void* const* recv, size_t count, int nranks,
                                         int group_size, gc_dtype t, gc_op op, gc_order order, hipStream_t stream) {
   if (!valid_dtype(t) || !valid_op(op) || !valid_order(order) || !send || !recv) return GC_ERR_INVALID_ARG;
-  GC_TRY(check_mesh(nranks, group_size, order, t));
+  GC_TRY(check_mesh(nranks, group_size));
   if (op == GC_AVG && t == GC_INT32) return GC_ERR_UNSUPPORTED;
   if (mul_overflows(count, 4)) return GC_ERR_INVALID_ARG;
   if (count == 0) return GC_OK;
@@ -344,6 +343,7 @@ extern "C" gc_status gc_hier_all_reduce(const void* const* send, void* const* re
     for (int i = 0; i < nranks; ++i)
       if (overlaps(outs[r], span(send[i], bytes)) && addr(recv[r]) != addr(send[i])) return GC_ERR_INVALID_ARG;
   gci::HierCall call{send, recv, nranks, group_size, count, t, t, op == GC_AVG, order != GC_ORDER_RANK, stream};
+  call.wire = order == GC_ORDER_RING_WIRE;
   return gci::launch_hier_all_reduce(call);
 }
 
@@ -352,7 +352,7 @@ extern "C" gc_status gc_hsdp_reduce_scatter(const void* const* send, void* const
                                             gc_order order, hipStream_t stream) {
   if (!valid_dtype(in_t) || !valid_dtype(out_t) || !valid_op(op) || !valid_order(order) || !send || !recv)
     return GC_ERR_INVALID_ARG;
-  GC_TRY(check_mesh(nranks, group_size, order, in_t));
+  GC_TRY(check_mesh(nranks, group_size));
   if ((in_t == GC_INT32) != (out_t == GC_INT32)) return GC_ERR_UNSUPPORTED;
   if (op == GC_AVG && in_t == GC_INT32) return GC_ERR_UNSUPPORTED;
   const uint64_t S = static_cast<uint64_t>(group_size);
@@ -377,6 +377,7 @@ extern "C" gc_status gc_hsdp_reduce_scatter(const void* const* send, void* const
   }
   gci::HierCall call{send, recv, nranks, group_size, S * recv_count, in_t, out_t, op == GC_AVG,
                      order != GC_ORDER_RANK, stream};
+  call.wire = order == GC_ORDER_RING_WIRE;
   return gci::launch_hsdp_reduce_scatter(call);
 }
 
@@ -785,7 +786,6 @@ extern "C" gc_status gc_bucket_all_reduce(const gc_bucket_plan* p, int bucket, v
       !valid_order(order))
     return GC_ERR_INVALID_ARG;
   if (p->t == GC_INT32 && (op == GC_AVG || sumsq)) return GC_ERR_UNSUPPORTED;
-  if (p->t == GC_BF16 && order == GC_ORDER_RING_WIRE) return GC_ERR_UNSUPPORTED;
   if (sumsq && addr(sumsq) % 8) return GC_ERR_INVALID_ARG;
   const size_t T = p->numel.size();
   const size_t es = p->es;
@@ -825,6 +825,7 @@ extern "C" gc_status gc_bucket_all_reduce(const gc_bucket_plan* p, int bucket, v
   }
   gci::BucketCall call{slot_ptrs.data(), static_cast<int>(slot), nranks, pieces.data(),
                        static_cast<int>(pieces.size()), p->t, op == GC_AVG, sumsq, stream};
+  call.wire = order == GC_ORDER_RING_WIRE;
   return gci::launch_bucket_all_reduce(call);
 }
 

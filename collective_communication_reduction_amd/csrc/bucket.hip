@@ -7,6 +7,11 @@
 // result is therefore bit-identical to packing the bucket, all-reducing it and
 // unpacking it, with a third of the HBM traffic: 2*N*B bytes instead of 6*N*B.
 //
+// With the bf16 wire order every forwarded partial is rounded to bf16 before
+// the next rank adds its term, as a ring that communicates in the gradients'
+// type would (DTLM §11), so the result stays bit-identical to pack ->
+// all-reduce (wire order) -> unpack.
+//
 // The host cuts the bucket into pieces (tensor x owner chunk); each piece has
 // one pointer set, one fold start and one alignment phase, so the inner loop
 // is the fused all-reduce's: 16-byte vectors, all of a batch's loads issued
@@ -92,7 +97,7 @@ __device__ __forceinline__ void group_atomic_add(double* dst, double v) {
   }
 }
 
-template <class In, class Out, int NF, int U, bool GUARD, bool SUMSQ, int P, int MAXS>
+template <class In, class Out, int NF, int U, bool GUARD, bool SUMSQ, bool WIRE, int P, int MAXS>
 __device__ __forceinline__ double bucket_tile(const BucketArgs<P, MAXS>& a, const PieceDev& pc, uint32_t N,
                                               uint64_t tv0, uint64_t nvec) {
   constexpr int VE = In::VE;
@@ -105,7 +110,7 @@ __device__ __forceinline__ double bucket_tile(const BucketArgs<P, MAXS>& a, cons
     off[u] = (pc.lo + pc.phase + v * VE) * In::ES;
   }
   Acc acc[U][VE];
-  fold_vec<In, NF, U>(in, pc.first, N, off, acc);
+  fold_vec<In, NF, U, WIRE>(in, pc.first, N, off, acc);
   const bool avg = a.avg != 0;
   double sq = 0.0;
 #pragma unroll
@@ -129,7 +134,7 @@ __device__ __forceinline__ double bucket_tile(const BucketArgs<P, MAXS>& a, cons
   return sq;
 }
 
-template <class In, class Out, int NF, int U, bool SUMSQ, int P, int MAXS>
+template <class In, class Out, int NF, int U, bool SUMSQ, bool WIRE, int P, int MAXS>
 __global__ void __launch_bounds__(kThreads) bucket_ar_kernel(const BucketArgs<P, MAXS> a, double* sumsq) {
   constexpr int VE = In::VE;
   constexpr int TV = kThreads * U;
@@ -146,9 +151,9 @@ __global__ void __launch_bounds__(kThreads) bucket_ar_kernel(const BucketArgs<P,
       const uint64_t nvec = pc.len > pc.phase ? (pc.len - pc.phase) / VE : 0;
       const uint64_t tv0 = static_cast<uint64_t>(t) * TV;
       if (tv0 + TV <= nvec) {
-        sq += bucket_tile<In, Out, NF, U, false, SUMSQ>(a, pc, N, tv0, nvec);
+        sq += bucket_tile<In, Out, NF, U, false, SUMSQ, WIRE>(a, pc, N, tv0, nvec);
       } else if (tv0 < nvec) {
-        sq += bucket_tile<In, Out, NF, U, true, SUMSQ>(a, pc, N, tv0, nvec);
+        sq += bucket_tile<In, Out, NF, U, true, SUMSQ, WIRE>(a, pc, N, tv0, nvec);
       }
       if (t == 0) {
         // elements before the first and after the last aligned vector: < 2 * VE
@@ -157,7 +162,7 @@ __global__ void __launch_bounds__(kThreads) bucket_ar_kernel(const BucketArgs<P,
         const uint64_t nscalar = nhead + (pc.len - tail_beg);
         if (threadIdx.x < nscalar) {
           const uint64_t E = pc.lo + (threadIdx.x < nhead ? threadIdx.x : tail_beg + (threadIdx.x - nhead));
-          const Acc x = finish(fold_one<In>(in, pc.first, N, E), avg, a.nf);
+          const Acc x = finish(fold_one<In, WIRE>(in, pc.first, N, E), avg, a.nf);
           for (uint32_t q = 0; q < N; ++q) put_one<Out>(a.ptr[pc.slot][q], E, x);
           if constexpr (SUMSQ) {
             const double y = stored_value<Out>(x);
@@ -171,7 +176,7 @@ __global__ void __launch_bounds__(kThreads) bucket_ar_kernel(const BucketArgs<P,
         const uint64_t e = static_cast<uint64_t>(t) * TE + u * kThreads + threadIdx.x;
         if (e < pc.len) {
           const uint64_t E = pc.lo + e;
-          const Acc x = finish(fold_one<In>(in, pc.first, N, E), avg, a.nf);
+          const Acc x = finish(fold_one<In, WIRE>(in, pc.first, N, E), avg, a.nf);
           for (uint32_t q = 0; q < N; ++q) put_one<Out>(a.ptr[pc.slot][q], E, x);
           if constexpr (SUMSQ) {
             const double y = stored_value<Out>(x);
@@ -199,17 +204,27 @@ gc_status launch(K kernel, const A& args, double* sumsq, hipStream_t stream) {
   return gci::hip_status(e);
 }
 
-template <class In, class Out, int P, int MAXS, bool SUMSQ>
+template <class In, class Out, int P, int MAXS, bool SUMSQ, bool WIRE>
 gc_status dispatch(const BucketArgs<P, MAXS>& a, double* sumsq, hipStream_t s) {
   if constexpr (P == 8) {
     switch (a.N) {
-      case 2: return launch(bucket_ar_kernel<In, Out, 2, kU, SUMSQ, P, MAXS>, a, sumsq, s);
-      case 4: return launch(bucket_ar_kernel<In, Out, 4, kU, SUMSQ, P, MAXS>, a, sumsq, s);
-      case 8: return launch(bucket_ar_kernel<In, Out, 8, kU, SUMSQ, P, MAXS>, a, sumsq, s);
+      case 2: return launch(bucket_ar_kernel<In, Out, 2, kU, SUMSQ, WIRE, P, MAXS>, a, sumsq, s);
+      case 4: return launch(bucket_ar_kernel<In, Out, 4, kU, SUMSQ, WIRE, P, MAXS>, a, sumsq, s);
+      case 8: return launch(bucket_ar_kernel<In, Out, 8, kU, SUMSQ, WIRE, P, MAXS>, a, sumsq, s);
       default: break;
     }
   }
-  return launch(bucket_ar_kernel<In, Out, 0, kU, SUMSQ, P, MAXS>, a, sumsq, s);
+  return launch(bucket_ar_kernel<In, Out, 0, kU, SUMSQ, WIRE, P, MAXS>, a, sumsq, s);
+}
+
+// The wire-rounding instantiations exist for bf16 data only (fp32 and int32
+// partials travel unrounded, so the plain kernels run).
+template <class In, class Out, int P, int MAXS, bool SUMSQ>
+gc_status dispatch_wire(const BucketArgs<P, MAXS>& a, bool wire, double* sumsq, hipStream_t s) {
+  if constexpr (In::ES == 2) {
+    if (wire) return dispatch<In, Out, P, MAXS, SUMSQ, true>(a, sumsq, s);
+  }
+  return dispatch<In, Out, P, MAXS, SUMSQ, false>(a, sumsq, s);
 }
 
 // One launch over pieces [p0, p1), whose slots are [s0, s1).
@@ -249,9 +264,9 @@ gc_status run_batch(const gci::BucketCall& c, int p0, int p1, int s0, int s1) {
   a.avg = c.avg ? 1u : 0u;
   a.nf = static_cast<float>(N);
   if constexpr (__is_same(typename In::Acc, float)) {
-    if (c.sumsq) return dispatch<In, Out, P, MAXS, true>(a, c.sumsq, c.stream);
+    if (c.sumsq) return dispatch_wire<In, Out, P, MAXS, true>(a, c.wire, c.sumsq, c.stream);
   }
-  return dispatch<In, Out, P, MAXS, false>(a, nullptr, c.stream);
+  return dispatch_wire<In, Out, P, MAXS, false>(a, c.wire, nullptr, c.stream);
 }
 
 template <class In, class Out, int P, int MAXS>

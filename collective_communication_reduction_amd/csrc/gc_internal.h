@@ -54,6 +54,7 @@ struct HierCall {
   bool avg;
   bool ring;
   hipStream_t stream;
+  bool wire = false;  // ring whose forwarded partials are rounded to the input type (both levels)
 };
 
 gc_status launch_hier_all_reduce(const HierCall& call);
@@ -81,6 +82,7 @@ struct BucketCall {
   bool avg;
   double* sumsq;  // device accumulator for the sum of squared results, or nullptr
   hipStream_t stream;
+  bool wire = false;  // ring whose forwarded partials are rounded to the input type
 };
 
 gc_status launch_bucket_all_reduce(const BucketCall& call);

@@ -14,6 +14,10 @@
 //   that chunk's R pieces; the groups are folded in ring order from h+1, each
 //   group's S members in ring order from i+1 (GC_ORDER_RANK: 0, 1, ... at
 //   both levels); fp32 partials throughout; one epilogue (avg divides by N).
+//   With the bf16 wire (DTLM §11: low-precision communication, fp32
+//   arithmetic) every partial is rounded to bf16 where the schedule sends it:
+//   inside a group before the next member adds its term, across groups before
+//   the next group adds its own (unrounded) partial.
 //
 // The grid walks cells (i, h); a tile holds U 16-byte vectors per thread of
 // one cell, so both fold starts are wavefront-uniform; the rank pointers are
@@ -70,33 +74,33 @@ __device__ __forceinline__ CellGeom cell_geom(const HierArgs<P>& a, uint32_t i, 
 // `in` is the workgroup's LDS copy of the rank pointers: indexing the kernel
 // arguments inside the runtime loop over groups made the compiler copy the
 // whole argument block to scratch memory.
-template <class In, int NS, int U, int P>
+template <class In, int NS, int U, bool WIRE, int P>
 __device__ __forceinline__ void fold2_vec(const HierArgs<P>& a, const char* const* in, uint32_t g0, uint32_t m0,
                                           const uint64_t (&off)[U], typename In::Acc (&acc)[U][In::VE]) {
   constexpr int VE = In::VE;
   typedef typename In::Acc Acc;
   const uint32_t S = NS ? NS : a.S;
   uint32_t g = g0;
-  fold_vec<In, NS, U>(in, m0, S, off, acc, g * S);
+  fold_vec<In, NS, U, WIRE>(in, m0, S, off, acc, g * S);
   for (uint32_t q = 1; q < a.R; ++q) {
     g = next_rank(g, a.R);
     Acc part[U][VE];
-    fold_vec<In, NS, U>(in, m0, S, off, part, g * S);
+    fold_vec<In, NS, U, WIRE>(in, m0, S, off, part, g * S);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int l = 0; l < VE; ++l) acc[u][l] = acc[u][l] + part[u][l];
+      for (int l = 0; l < VE; ++l) acc[u][l] = on_wire<In, WIRE>(acc[u][l]) + part[u][l];
   }
 }
 
-template <class In, int P>
+template <class In, bool WIRE, int P>
 __device__ __forceinline__ typename In::Acc fold2_one(const HierArgs<P>& a, const char* const* in, uint32_t g0,
                                                       uint32_t m0, uint64_t E) {
   uint32_t g = g0;
-  typename In::Acc acc = fold_one<In>(in, m0, a.S, E, g * a.S);
+  typename In::Acc acc = fold_one<In, WIRE>(in, m0, a.S, E, g * a.S);
   for (uint32_t q = 1; q < a.R; ++q) {
     g = next_rank(g, a.R);
-    acc = acc + fold_one<In>(in, m0, a.S, E, g * a.S);
+    acc = on_wire<In, WIRE>(acc) + fold_one<In, WIRE>(in, m0, a.S, E, g * a.S);
   }
   return acc;
 }
@@ -108,7 +112,7 @@ __device__ __forceinline__ void load_rank_pointers(const HierArgs<P>& a, const c
   __syncthreads();
 }
 
-template <int KIND, class In, class Out, int NS, int U, bool GUARD, int P>
+template <int KIND, class In, class Out, int NS, int U, bool GUARD, bool WIRE, int P>
 __device__ __forceinline__ void hier_tile(const HierArgs<P>& a, const char* const* in, uint32_t i, uint32_t g0,
                                           uint32_t m0, const CellGeom& c, uint64_t tv0) {
   constexpr int VE = In::VE;
@@ -120,7 +124,7 @@ __device__ __forceinline__ void hier_tile(const HierArgs<P>& a, const char* cons
     off[u] = (a.phase + v * VE) * In::ES;
   }
   Acc acc[U][VE];
-  fold2_vec<In, NS, U>(a, in, g0, m0, off, acc);
+  fold2_vec<In, NS, U, WIRE>(a, in, g0, m0, off, acc);
   const bool avg = a.avg != 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -154,7 +158,7 @@ __device__ __forceinline__ void hier_tile(const HierArgs<P>& a, const char* cons
   }
 }
 
-template <int KIND, class In, class Out, int NS, int U, int P>
+template <int KIND, class In, class Out, int NS, int U, bool WIRE, int P>
 __global__ void __launch_bounds__(kThreads) hier_vec_kernel(const HierArgs<P> a) {
   constexpr int VE = In::VE;
   constexpr int TV = kThreads * U;
@@ -172,9 +176,9 @@ __global__ void __launch_bounds__(kThreads) hier_vec_kernel(const HierArgs<P> a)
     const uint32_t m0 = a.ring ? next_rank(i, a.S) : 0;
     const uint64_t tv0 = c.vlo + static_cast<uint64_t>(t) * TV;
     if (tv0 + TV <= c.vhi) {
-      hier_tile<KIND, In, Out, NS, U, false>(a, s_in, i, g0, m0, c, tv0);
+      hier_tile<KIND, In, Out, NS, U, false, WIRE>(a, s_in, i, g0, m0, c, tv0);
     } else if (tv0 < c.vhi) {
-      hier_tile<KIND, In, Out, NS, U, true>(a, s_in, i, g0, m0, c, tv0);
+      hier_tile<KIND, In, Out, NS, U, true, WIRE>(a, s_in, i, g0, m0, c, tv0);
     }
     if (t == 0) {
       // Elements of the cell outside its aligned vectors: at most 2*VE - 2.
@@ -185,7 +189,7 @@ __global__ void __launch_bounds__(kThreads) hier_vec_kernel(const HierArgs<P> a)
       const uint64_t nscalar = nhead + (c.hi - tail_beg);
       if (threadIdx.x < nscalar) {
         const uint64_t E = threadIdx.x < nhead ? c.lo + threadIdx.x : tail_beg + (threadIdx.x - nhead);
-        const Acc x = finish(fold2_one<In>(a, s_in, g0, m0, E), avg, a.nf);
+        const Acc x = finish(fold2_one<In, WIRE>(a, s_in, g0, m0, E), avg, a.nf);
         if constexpr (KIND == kHierAllReduce) {
           for (uint32_t q = 0; q < a.N; ++q) put_one<Out>(a.out[q], E, x);
         } else {
@@ -197,7 +201,7 @@ __global__ void __launch_bounds__(kThreads) hier_vec_kernel(const HierArgs<P> a)
 }
 
 // Element-wise variant for buffers whose relative alignment rules out vectors.
-template <int KIND, class In, class Out, int P>
+template <int KIND, class In, class Out, bool WIRE, int P>
 __global__ void __launch_bounds__(kThreads) hier_elem_kernel(const HierArgs<P> a) {
   constexpr int TE = kThreads * 4;
   __shared__ const char* s_in[P];
@@ -215,7 +219,7 @@ __global__ void __launch_bounds__(kThreads) hier_elem_kernel(const HierArgs<P> a
     for (int u = 0; u < 4; ++u) {
       const uint64_t E = c.lo + static_cast<uint64_t>(t) * TE + u * kThreads + threadIdx.x;
       if (E < c.hi) {
-        const typename In::Acc x = finish(fold2_one<In>(a, s_in, g0, m0, E), avg, a.nf);
+        const typename In::Acc x = finish(fold2_one<In, WIRE>(a, s_in, g0, m0, E), avg, a.nf);
         if constexpr (KIND == kHierAllReduce) {
           for (uint32_t q = 0; q < a.N; ++q) put_one<Out>(a.out[q], E, x);
         } else {
@@ -298,16 +302,26 @@ HierArgs<P> make_args(const gci::HierCall& c) {
   return a;
 }
 
-template <int KIND, class In, class Out, int U, int P>
+template <int KIND, class In, class Out, int U, bool WIRE, int P>
 gc_status run_p(const gci::HierCall& c, bool vec, uint32_t phase, uint32_t tpc) {
   HierArgs<P> a = make_args<P>(c);
   a.phase = phase;
   a.tpc = tpc;
   a.ntiles = static_cast<uint32_t>(c.nranks) * tpc;  // S * R cells
-  if (!vec) return launch(hier_elem_kernel<KIND, In, Out, P>, a, a.ntiles, c.stream);
-  if (c.group == 8) return launch(hier_vec_kernel<KIND, In, Out, 8, U, P>, a, a.ntiles, c.stream);
-  if (c.group == 4) return launch(hier_vec_kernel<KIND, In, Out, 4, U, P>, a, a.ntiles, c.stream);
-  return launch(hier_vec_kernel<KIND, In, Out, 0, U, P>, a, a.ntiles, c.stream);
+  if (!vec) return launch(hier_elem_kernel<KIND, In, Out, WIRE, P>, a, a.ntiles, c.stream);
+  if (c.group == 8) return launch(hier_vec_kernel<KIND, In, Out, 8, U, WIRE, P>, a, a.ntiles, c.stream);
+  if (c.group == 4) return launch(hier_vec_kernel<KIND, In, Out, 4, U, WIRE, P>, a, a.ntiles, c.stream);
+  return launch(hier_vec_kernel<KIND, In, Out, 0, U, WIRE, P>, a, a.ntiles, c.stream);
+}
+
+// The wire-rounding kernels exist for bf16 inputs only; for the other types
+// the rounding is an identity and the plain kernels run.
+template <int KIND, class In, class Out, int U, int P>
+gc_status run_w(const gci::HierCall& c, bool vec, uint32_t phase, uint32_t tpc) {
+  if constexpr (In::ES == 2) {
+    if (c.wire) return run_p<KIND, In, Out, U, true, P>(c, vec, phase, tpc);
+  }
+  return run_p<KIND, In, Out, U, false, P>(c, vec, phase, tpc);
 }
 
 template <int KIND, class In, class Out>
@@ -341,11 +355,11 @@ gc_status run(const gci::HierCall& c) {
   const bool small = vec && kU > 1 && static_cast<uint64_t>(tpc) * N < kSmallTiles;
   if (small) {
     tpc = static_cast<uint32_t>(std::max<uint64_t>(1, (most + kThreads - 1) / kThreads));
-    return N <= 8 ? run_p<KIND, In, Out, 1, 8>(c, vec, phase, tpc)
-                  : run_p<KIND, In, Out, 1, GC_MAX_RANKS>(c, vec, phase, tpc);
+    return N <= 8 ? run_w<KIND, In, Out, 1, 8>(c, vec, phase, tpc)
+                  : run_w<KIND, In, Out, 1, GC_MAX_RANKS>(c, vec, phase, tpc);
   }
-  return N <= 8 ? run_p<KIND, In, Out, kU, 8>(c, vec, phase, tpc)
-                : run_p<KIND, In, Out, kU, GC_MAX_RANKS>(c, vec, phase, tpc);
+  return N <= 8 ? run_w<KIND, In, Out, kU, 8>(c, vec, phase, tpc)
+                : run_w<KIND, In, Out, kU, GC_MAX_RANKS>(c, vec, phase, tpc);
 }
 
 template <int KIND>

@@ -300,12 +300,14 @@ def test_fsdp2_validation():
     assert _status(ag, S_, P_, **dict(akw, dtype=9)) == gc.GC_ERR_INVALID_ARG
 
 
-def test_wire_order_rejected_for_bf16_buckets():
+def test_wire_order_validated_like_the_others_for_buckets():
+    # the bf16 wire order is accepted by the bucket all-reduce; its arguments are checked as usual
     plan = gc.BucketPlan([8, 8], "bf16", 1 << 20)
     try:
         ptrs = _ptrs(4)
-        assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, ptrs, 2, order="ring_wire",
-                       stream=0) == gc.GC_ERR_UNSUPPORTED
+        assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, ptrs[:3] + [0], 2, order="ring_wire",
+                       stream=0) == gc.GC_ERR_INVALID_ARG
+        assert _status(gc.gc_bucket_all_reduce, plan.handle, 0, ptrs, 2, order=7, stream=0) == gc.GC_ERR_INVALID_ARG
     finally:
         plan.close()
 
@@ -316,7 +318,8 @@ def test_hier_and_hsdp_validation():
     assert _status(har, s, r, 4, count=0, dtype="bf16", stream=0) == gc.GC_OK
     assert _status(har, s, r, 3, count=16, dtype="bf16", stream=0) == gc.GC_ERR_INVALID_ARG     # 3 does not divide 8
     assert _status(har, s, r, 0, count=16, dtype="bf16", stream=0) == gc.GC_ERR_INVALID_ARG
-    assert _status(har, s, r, 4, count=16, dtype="bf16", order="ring_wire", stream=0) == gc.GC_ERR_UNSUPPORTED
+    assert _status(har, s, r, 3, count=16, dtype="bf16", order="ring_wire", stream=0) == gc.GC_ERR_INVALID_ARG
+    assert _status(har, s, r, 4, count=0, dtype="bf16", order="ring_wire", stream=0) == gc.GC_OK
     assert _status(har, s, r, 4, count=16, dtype="int32", op="avg", stream=0) == gc.GC_ERR_UNSUPPORTED
     assert _status(har, s, r[:7] + [r[6] + 8], 4, count=16, dtype="fp32", stream=0) == gc.GC_ERR_INVALID_ARG
     assert _status(har, s, r[:7] + [s[3] + 4], 4, count=16, dtype="fp32", stream=0) == gc.GC_ERR_INVALID_ARG

@@ -1,7 +1,8 @@
 """GPU parity of the two-level all-reduce and the HSDP reduce-scatter (AIG6
 Table 6-2, AIG6 §6.3.6, DTLM §4) against the oracle's three emulated rings,
 element by element: group shapes from 1 x N to N x 1, ragged counts, all type
-pairs, both orders, misaligned views and in place."""
+pairs, the ring, rank and bf16-wire orders (DTLM §11), misaligned views and in
+place."""
 
 import numpy as np
 import pytest
@@ -35,7 +36,7 @@ SHAPES = [(2, 8, 8 * 4096 * 2 + 13), (2, 4, 1000), (4, 2, 37), (3, 5, 12345), (8
 
 @pytest.mark.parametrize("R,S,count", SHAPES)
 @pytest.mark.parametrize("dtype,op", [("bf16", "avg"), ("fp32", "sum"), ("int32", "sum")])
-@pytest.mark.parametrize("order", ["ring", "rank"])
+@pytest.mark.parametrize("order", ["ring", "rank", "ring_wire"])
 def test_hier_all_reduce(R, S, count, dtype, op, order):
     N = R * S
     xs = _gen(dtype, N, count, seed=R * 31 + S + count)
@@ -51,7 +52,7 @@ def test_hier_all_reduce(R, S, count, dtype, op, order):
 @pytest.mark.parametrize("R,S,rc", [(2, 8, 4096 + 5), (4, 2, 9), (3, 4, 1), (2, 8, 64), (8, 8, 300)])
 @pytest.mark.parametrize("tin,tout,op", [("bf16", "fp32", "avg"), ("bf16", "bf16", "avg"), ("fp32", "bf16", "sum"),
                                          ("int32", "int32", "sum")])
-@pytest.mark.parametrize("order", ["ring", "rank"])
+@pytest.mark.parametrize("order", ["ring", "rank", "ring_wire"])
 def test_hsdp_reduce_scatter(R, S, rc, tin, tout, op, order):
     N = R * S
     xs = _gen(tin, N, S * rc, seed=R + S + rc)
@@ -65,18 +66,19 @@ def test_hsdp_reduce_scatter(R, S, rc, tin, tout, op, order):
 
 
 @pytest.mark.parametrize("offsets", [(1,) * 8, (0, 1, 2, 3, 4, 5, 6, 7)])
-def test_hier_misaligned_views(offsets):
+@pytest.mark.parametrize("order", ["ring", "ring_wire"])
+def test_hier_misaligned_views(offsets, order):
     R, S, count, dtype = 2, 4, 5000 + 3, "bf16"
     N = R * S
     xs = _gen(dtype, N, count, seed=7)
-    want = H.all_reduce(xs, S, dtype, "avg", "ring")[0]
+    want = H.all_reduce(xs, S, dtype, "avg", order)[0]
     bi = [empty(count + 8, dtype) for _ in range(N)]
     bo = [empty(count + 8, dtype) for _ in range(N)]
     send = [b[o:o + count] for b, o in zip(bi, offsets)]
     recv = [b[o:o + count] for b, o in zip(bo, offsets)]
     for v, x in zip(send, xs):
         v.copy_(to_dev(x, dtype))
-    gc.gc_hier_all_reduce(send, recv, S, op="avg")
+    gc.gc_hier_all_reduce(send, recv, S, op="avg", order=order)
     torch.cuda.synchronize()
     for r in range(N):
         assert_same(from_dev(recv[r]), want, dtype, f"rank {r}")

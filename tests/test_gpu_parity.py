@@ -346,7 +346,7 @@ def test_bucket_pack_unpack(dtype, cap, pad, seed):
 @pytest.mark.parametrize("dtype,op,N,pad,seed", [("bf16", "avg", 8, 1, 0), ("bf16", "avg", 3, 8, 1), ("fp32", "sum", 2, 1, 2),
                                                  ("fp32", "avg", 16, 16, 3), ("int32", "sum", 4, 1, 4),
                                                  ("bf16", "sum", 1, 1, 5), ("bf16", "avg", 64, 64, 6)])
-@pytest.mark.parametrize("order", ["ring", "rank"])
+@pytest.mark.parametrize("order", ["ring", "rank", "ring_wire"])
 def test_bucket_all_reduce_zero_copy(dtype, op, N, pad, seed, order):
     # in place over the tensors; must equal pack -> all-reduce -> unpack of the oracle bit for bit
     rng = np.random.default_rng(seed)

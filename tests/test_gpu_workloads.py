@@ -2,13 +2,19 @@
 HBM layout bench.py times (a RankArena: each rank's buffers in its own region
 of HBM, the workload's stagger between ranks: 4 KiB, 64 KiB for 16 ranks).
 
-At these sizes the step-by-step oracle cannot hold the inputs, so each test
-checks (a) sampled outputs the oracle computes one by one from inputs it
-regenerates on the host by index (random positions plus every chunk edge),
-and (b) properties that hold at any size, checked on the device: every rank's
-result is identical, fused == reduce-scatter + all-gather bit for bit, and
-data movement equals the permutation the oracle derives.  The 4-rank fp32
-all-reduce is small enough for a full oracle comparison."""
+At these sizes the step-by-step oracle cannot hold the inputs at once.  The
+reductions of the all-reduce, FSDP, two-level and HSDP workloads are still
+compared with the oracle element by element: the inputs of one owner chunk
+(one cell of the two-level schedule) at a time are copied back from the
+device generator's buffers (its bits are pinned to the host generator's) and
+folded by the oracle's whole-chunk evaluators, which are themselves pinned to
+the step-by-step emulation.  The DDP and MoE workloads check sampled outputs
+the oracle computes one by one from inputs it regenerates on the host by index
+(random positions plus every chunk edge).  Properties that hold at any size are
+checked on the device as well: every rank's result is identical, fused ==
+reduce-scatter + all-gather bit for bit, and data movement equals the
+permutation the oracle derives.  The 4-rank fp32 all-reduce is small enough for
+a full step-by-step oracle comparison."""
 
 import numpy as np
 import pytest
@@ -52,6 +58,11 @@ def _gather(t, pos):
     return from_dev(t.index_select(0, idx))
 
 
+def _slices(bufs, lo, hi):
+    """Host copy of elements [lo, hi) of every rank's buffer, one row per rank."""
+    return list(from_dev(torch.stack([b[lo:hi] for b in bufs])))
+
+
 def test_ar_fp32_n4_full():
     cfg = WORKLOADS["ar_fp32_n4"]
     N, S = cfg["nranks"], cfg["count"]
@@ -88,12 +99,18 @@ def test_ar_bf16_n8_full():
     for r in range(N):
         assert torch.equal(recv[r].view(torch.int16), recv[0].view(torch.int16)), f"rank {r} differs"
         assert torch.equal(recv2[r].view(torch.int16), recv[0].view(torch.int16)), f"rs_ag rank {r} differs"
-    pos = _positions(S, N, np.random.default_rng(1))
+    # every output, owner chunk by owner chunk (rank 3's copy; all ranks are equal above)
+    c = -(-S // N)
+    for j in range(N):
+        lo, hi = min(S, j * c), min(S, (j + 1) * c)
+        want = SM.reduce_scatter_owner(_slices(send, lo, hi), j, "bf16", "bf16", "avg", "ring")
+        got = from_dev(recv[3][lo:hi])
+        assert max_ulp(got, want) <= 1
+        assert_same(got, want, "bf16", f"chunk {j}")
+    # and sampled positions against inputs the oracle regenerates on the host
+    pos = _positions(S, N, np.random.default_rng(1), m=1 << 14)
     vals = np.stack([G.normal_bf16(keys[r], pos, sigma) for r in range(N)])
-    want = SM.all_reduce_at(vals, pos, S, "bf16", "avg", "ring")
-    got = _gather(recv[3], pos)
-    assert max_ulp(got, want) <= 1
-    assert_same(got, want, "bf16", "sampled outputs")
+    assert_same(_gather(recv[3], pos), SM.all_reduce_at(vals, pos, S, "bf16", "avg", "ring"), "bf16", "sampled")
 
 
 def _llama_layout():
@@ -204,9 +221,13 @@ def test_fsdp_layer_n64_full():
     gshards = arena.alloc(rc, "fp32")
     gc.gc_reduce_scatter(grads, gshards, op="avg", order="ring")
     torch.cuda.synchronize()
+    # all 64 x 3,162,240 fp32 outputs, streamed owner by owner through the oracle
+    for j in range(N):
+        want = SM.reduce_scatter_owner(_slices(grads, j * rc, (j + 1) * rc), j, "bf16", "fp32", "avg", "ring")
+        assert_same(from_dev(gshards[j]), want, "fp32", f"reduce-scatter owner {j}")
     rng = np.random.default_rng(3)
-    for j in list(range(0, N, 7)) + [N - 1]:
-        k = np.unique(np.concatenate([rng.integers(0, rc, size=2048), [0, 1, rc - 2, rc - 1]]))
+    for j in (0, 29, N - 1):                            # a sample against host-regenerated inputs too
+        k = np.unique(np.concatenate([rng.integers(0, rc, size=512), [0, 1, rc - 2, rc - 1]]))
         vals = np.stack([G.normal_bf16(gkeys[i], j * rc + k, 1e-3) for i in range(N)])
         want = SM.reduce_scatter_at(vals, np.full(len(k), j), k, rc, "bf16", "fp32", "avg", "ring")
         assert_same(_gather(gshards[j], k), want, "fp32", f"reduce-scatter owner {j}")
@@ -218,6 +239,9 @@ def test_fsdp_layer_n64_full():
     torch.cuda.synchronize()
     for d in range(1, N):
         assert torch.equal(params[d].view(torch.int16), params[0].view(torch.int16)), f"rank {d} differs"
+    # every output: the all-gather's result is the concatenation of the shards in rank order
+    for j in range(N):
+        assert torch.equal(params[0][j * rc:(j + 1) * rc].view(torch.int16), pshards[j].view(torch.int16)), j
     pos = _positions(S, N, np.random.default_rng(4), m=1 << 16)
     owner, k = pos // rc, pos % rc
     want = np.array([G.normal_bf16(pkeys[i], np.array([kk]), 0.02)[0] for i, kk in zip(owner, k)], dtype=np.uint16)
@@ -469,12 +493,27 @@ def test_wire_bf16_ring_error_study():
     assert stats["ring_wire64"][0] > 10 * stats["ring64"][0] and stats["ring_wire64"][2] > stats["ring64"][2]
 
 
+def _cells(count, S, R, chunk=None):
+    """(i, h, lo, hi) of every cell of the two-level schedule: chunk i of S, cross-group piece h of R."""
+    c1 = chunk if chunk is not None else -(-count // S)
+    out = []
+    for i in range(S):
+        lo, hi = min(count, i * c1), min(count, (i + 1) * c1)
+        c2 = max(1, -(-(hi - lo) // R))
+        for h in range(R):
+            a, b = lo + min(hi - lo, h * c2), lo + min(hi - lo, (h + 1) * c2)
+            if a < b:
+                out.append((i, h, a, b))
+    return out
+
+
 def test_hier_ar_n16_and_hsdp_layer_full():
     """Two nodes of eight (AIG6 §6.3.6's HSDP example) at full size: the
     two-level all-reduce of 16 x 64 MiB bf16 (avg) and the HSDP reduce-scatter
-    of one transformer layer (bf16 -> fp32 avg), sampled against the oracle's
-    two-level fold; every rank's all-reduce result is identical and the shard
-    each group holds is the same."""
+    of one transformer layer (bf16 -> fp32 avg), every output compared with the
+    oracle's two-level fold cell by cell (plus a sample against host-regenerated
+    inputs); every rank's all-reduce result is identical and the shard each
+    group holds is the same."""
     cfg = WORKLOADS["hier_ar_n16"]
     N, S, count = cfg["nranks"], cfg["group"], cfg["count"]
     R = N // S
@@ -497,12 +536,15 @@ def test_hier_ar_n16_and_hsdp_layer_full():
         for h in range(R):
             a, b = lo + min(L, h * c2), lo + min(L, (h + 1) * c2)
             edges += [a, a + 1, b - 2, b - 1]
-    pos = np.unique(np.concatenate([np.random.default_rng(31).integers(0, count, size=1 << 17), edges]))
+    pos = np.unique(np.concatenate([np.random.default_rng(31).integers(0, count, size=1 << 14), edges]))
     pos = pos[(pos >= 0) & (pos < count)]
     vals = np.stack([G.normal_bf16(keys[r], pos, cfg["sigma"]) for r in range(N)])
     g0, m0 = SM.hier_fold_starts(pos, count, S, R, "ring")
     want = SM.hier_reduce_positions(vals, S, g0, m0, "bf16", "avg", "bf16")
     assert_same(_gather(recv[5], pos), want, "bf16", "two-level all-reduce")
+    for i, h, a, b in _cells(count, S, R):                     # every output, cell by cell
+        want = SM.hier_reduce_block(_slices(send, a, b), S, (h + 1) % R, (i + 1) % S, "bf16", "avg", "bf16")
+        assert_same(from_dev(recv[5][a:b]), want, "bf16", f"two-level cell ({i}, {h})")
     del send, recv, arena                                     # release the first arena before the second
     torch.cuda.empty_cache()
 
@@ -527,3 +569,88 @@ def test_hier_ar_n16_and_hsdp_layer_full():
         g0, m0 = SM.hier_fold_starts(p, Sflat, S, R, "ring", chunk=rc)
         want = SM.hier_reduce_positions(vals, S, g0, m0, "bf16", "avg", "fp32")
         assert_same(_gather(shards[S + i], k), want, "fp32", f"hsdp member {i}")
+    for i, h, a, b in _cells(Sflat, S, R, chunk=rc):           # every output, cell by cell
+        want = SM.hier_reduce_block(_slices(grads, a, b), S, (h + 1) % R, (i + 1) % S, "bf16", "avg", "fp32")
+        assert_same(from_dev(shards[S + i][a - i * rc:b - i * rc]), want, "fp32", f"hsdp cell ({i}, {h})")
+
+
+def test_wire_bf16_error_study_ddp_and_hsdp():
+    """The bf16-wire ring against the fp32-partial ring on two more paths at
+    full size: the DDP step's 226 zero-copy bucket all-reduces of the Llama-7B
+    gradient set (8 ranks, avg) and the HSDP reduce-scatter of one layer on 2 x 8
+    ranks (avg, bf16 -> fp32).  Sampled outputs of both orders are bit-exact
+    against the oracle's folds in that order; the errors against the exact mean
+    are printed, and the wire's must be the larger (DTLM §11)."""
+    from oracle.numerics import bf16_to_f32
+    cfg = WORKLOADS["ddp_llama7b"]
+    N, sigma, cap = cfg["nranks"], cfg["sigma"], cfg["cap_bytes"]
+    numels, offs = _llama_layout()
+    total = int(offs[-1])
+    keys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    arena = gc.RankArena(N, min_bytes=total * 2 + (1 << 30))
+    flat = arena.alloc(total, "bf16")
+    tensors = [flat[r][int(offs[t]):int(offs[t]) + numels[t]] for r in range(N) for t in range(len(numels))]
+    ptrs = gc.gc_pointers(tensors)
+    plan = gc.BucketPlan(numels, "bf16", cap, reverse=True)
+    oracle_buckets = OB.assign_buckets(numels, 2, cap, reverse=True)
+    rng = np.random.default_rng(23)
+    samples = []                                    # (bucket positions, model-order flat indices, used)
+    for ts in oracle_buckets:
+        boffs, used, _ = OB.bucket_layout(ts, numels)
+        e = np.unique(np.concatenate([rng.integers(0, used, size=256), [0, used - 1]]))
+        which = np.searchsorted(np.asarray(boffs), e, side="right") - 1
+        samples.append((e, np.array([offs[ts[w]] + (ee - boffs[w]) for w, ee in zip(which, e)], np.int64), used))
+    vals = [np.stack([G.normal_bf16(keys[r], f, sigma) for r in range(N)]) for _, f, _ in samples]
+    stats = {}
+    for order in ("ring", "ring_wire"):
+        for r in range(N):                          # fresh gradients: the all-reduce runs in place
+            GD.fill_normal_bf16(flat[r], keys[r], sigma)
+        for b in range(plan.nbuckets):
+            plan.all_reduce(b, ptrs, N, op="avg", order=order)
+        torch.cuda.synchronize()
+        got = _gather(flat[6], np.concatenate([f for _, f, _ in samples]))
+        want = np.concatenate([SM.all_reduce_at(v, e, used, "bf16", "avg", order)
+                               for v, (e, _, used) in zip(vals, samples)])
+        assert_same(got, want, "bf16", f"ddp bucket all-reduce {order}")
+        wide = np.concatenate([bf16_to_f32(v).astype(np.float64) for v in vals], axis=1)
+        err, exact = _scaled_error(bf16_to_f32(got), wide, N)
+        off = float(np.mean(_bf16_nearest(exact) != got))
+        stats[order] = (off, float(np.median(err)), float(np.quantile(err, 0.99)), float(err.max()))
+        print(f"ddp_llama7b zero-copy {order}: differs from the correctly rounded mean {off:.4%}; error / mean|x|: "
+              f"median {stats[order][1]:.3e}, p99 {stats[order][2]:.3e}, max {stats[order][3]:.3e} "
+              f"({len(got)} samples over {plan.nbuckets} buckets)", flush=True)
+    assert stats["ring_wire"][1] > stats["ring"][1] and stats["ring_wire"][0] > stats["ring"][0]
+    plan.close()
+    del flat, tensors, ptrs, arena
+    torch.cuda.empty_cache()
+
+    hc = WORKLOADS["hsdp_layer_n16"]
+    N, S = hc["nranks"], hc["group"]
+    R = N // S
+    _, _, Sflat, _ = OB.flat_param_shards([n for _, n in fsdp_layer_tensors()], S)
+    rc = Sflat // S
+    keys = [G.stream_key(SEED, r, 0) for r in range(N)]
+    arena = gc.RankArena(N, stagger_bytes=hc["stagger"])
+    grads = arena.alloc(Sflat, "bf16")
+    for r in range(N):
+        GD.fill_normal_bf16(grads[r], keys[r], hc["grad_sigma"])
+    cells = [(i, h, a, b) for i, h, a, b in _cells(Sflat, S, R, chunk=rc)]
+    pos = [np.unique(np.concatenate([rng.integers(a, b, size=1024), [a, b - 1]])) for _, _, a, b in cells]
+    cvals = [np.stack([G.normal_bf16(keys[r], p, hc["grad_sigma"]) for r in range(N)]) for p in pos]
+    for order in ("ring", "ring_wire"):
+        shards = arena.alloc(rc, "fp32")
+        gc.gc_hsdp_reduce_scatter(grads, shards, S, op="avg", order=order)
+        torch.cuda.synchronize()
+        rel = []
+        for (i, h, a, b), p, v in zip(cells, pos, cvals):
+            want = SM.hier_reduce_block(list(v), S, (h + 1) % R, (i + 1) % S, "bf16", "avg", "fp32",
+                                        "bf16" if order == "ring_wire" else None)
+            got = _gather(shards[S + i], p - i * rc)
+            assert_same(got, want, "fp32", f"hsdp {order} cell ({i}, {h})")
+            rel.append(_scaled_error(got, bf16_to_f32(v).astype(np.float64), N)[0])
+        rel = np.concatenate(rel)
+        stats["hsdp_" + order] = (float(np.median(rel)), float(np.quantile(rel, 0.99)), float(rel.max()))
+        print(f"hsdp_layer_n16 {order}: error / mean|x|: median {stats['hsdp_' + order][0]:.3e}, "
+              f"p99 {stats['hsdp_' + order][1]:.3e}, max {stats['hsdp_' + order][2]:.3e} ({len(rel)} samples)",
+              flush=True)
+    assert stats["hsdp_ring_wire"][0] > 10 * stats["hsdp_ring"][0]
