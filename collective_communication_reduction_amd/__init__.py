@@ -82,6 +82,7 @@ _c_hsdp_rs = _sig("gc_hsdp_reduce_scatter", _int, _VPP, _VPP, _sz, _int, _int, _
 _c_fsdp2_ag = _sig("gc_fsdp2_all_gather", _int, _VPP, _VPP, _SZP, _SZP, _int, _int, _int, _vp)
 _c_moe_scratch = _sig("gc_moe_route_scratch_bytes", _sz, _I64P, _int, _int, _int)
 _c_moe_route = _sig("gc_moe_route", _int, _VPP, _I64P, _int, _int, _int, _vp, _VPP, _vp, _sz, _vp)
+_c_moe_route_noalloc = _sig("gc_moe_route_noalloc", _int, _VPP, _I64P, _int, _int, _int, _vp, _VPP, _vp)
 _c_moe_dispatch = _sig("gc_moe_dispatch", _int, _VPP, _I64P, _VPP, _int, _int, _sz, _VPP, _I64P, _vp)
 _c_moe_combine = _sig("gc_moe_combine", _int, _VPP, _I64P, _VPP, _VPP, _I64P, _int, _int, _sz, _int, _VPP, _vp)
 _c_plan_create = _sig("gc_bucket_plan_create", _int, ctypes.POINTER(ctypes.c_size_t), _int, _int, _sz, _int, _sz,
@@ -396,6 +397,23 @@ def gc_moe_route(experts, ntokens, topk, experts_per_rank, splits, dest, scratch
                         _bufs(dest, n, _per_route(ntokens, topk, 8), "dest"),
                         _buf(scratch, int(scratch_bytes), "scratch"), int(scratch_bytes), _stream(stream, splits)),
            "gc_moe_route")
+    return splits, dest
+
+
+GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def gc_moe_route_noalloc(experts, ntokens, topk, experts_per_rank, splits, dest, stream=None):
+    """gc_moe_route without a scratch argument, for callers that cannot allocate device
+    memory: the plan uses the library's static per-GPU scratch (at most
+    GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES; larger plans raise GcError with GC_ERR_UNSUPPORTED).
+    Calls that overlap on one GPU share that scratch and race."""
+    n = len(ntokens)
+    nsplit = n * n * max(0, int(experts_per_rank)) * 8
+    _check(_c_moe_route_noalloc(_bufs(experts, n, _per_route(ntokens, topk, 4), "experts"), _i64_array(ntokens), n,
+                                int(topk), int(experts_per_rank), _buf(splits, nsplit, "splits"),
+                                _bufs(dest, n, _per_route(ntokens, topk, 8), "dest"), _stream(stream, splits)),
+           "gc_moe_route_noalloc")
     return splits, dest
 
 

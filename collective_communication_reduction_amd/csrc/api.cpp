@@ -559,33 +559,70 @@ extern "C" size_t gc_moe_route_scratch_bytes(const int64_t* ntokens, int nranks,
   return moe_route_geom(ntokens, nranks, topk, experts_per_rank, g) == GC_OK ? g.bytes : 0;
 }
 
+namespace {
+
+// Checks shared by gc_moe_route and gc_moe_route_noalloc; the scratch span is
+// empty for the variant whose scratch is the library's own.  Nothing here
+// allocates (fixed-size span lists: at most 2 + nranks outputs and nranks
+// inputs), so the variant without a scratch argument allocates nothing at all.
+gc_status moe_route_check(const int32_t* const* experts, const int64_t* ntokens, int nranks, int topk,
+                          int experts_per_rank, const int64_t* splits, int32_t* const* dest, Span scratch) {
+  const int N = nranks, E = experts_per_rank;
+  if (!experts || !dest || !splits || addr(splits) % 8) return GC_ERR_INVALID_ARG;
+  Span outs[GC_MAX_RANKS + 2], ins[GC_MAX_RANKS];
+  int nout = 0, nin = 0;
+  outs[nout++] = span(splits, static_cast<uint64_t>(N) * N * E * 8);
+  outs[nout++] = scratch;
+  for (int s = 0; s < N; ++s) {
+    const int64_t routes = ntokens[s] * topk;
+    if (!routes) continue;
+    if (!experts[s] || addr(experts[s]) % 4 || !dest[s] || addr(dest[s]) % 8) return GC_ERR_INVALID_ARG;
+    ins[nin++] = span(experts[s], routes * 4);
+    outs[nout++] = span(dest[s], routes * 8);
+  }
+  std::sort(outs, outs + nout, [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  for (int k = 1; k < nout; ++k)
+    if (overlaps(outs[k - 1], outs[k])) return GC_ERR_INVALID_ARG;  // sorted: any overlap shows between neighbours
+  for (int o = 0; o < nout; ++o)
+    for (int i = 0; i < nin; ++i)
+      if (overlaps(outs[o], ins[i])) return GC_ERR_INVALID_ARG;
+  return GC_OK;
+}
+
+gc_status moe_route_launch(const int32_t* const* experts, const int64_t* ntokens, int nranks, int topk,
+                           int experts_per_rank, int64_t* splits, int32_t* const* dest, void* scratch,
+                           const MoeRouteGeom& g, hipStream_t stream) {
+  int64_t routes[GC_MAX_RANKS];
+  for (int s = 0; s < nranks; ++s) routes[s] = ntokens[s] * topk;
+  char* base = static_cast<char*>(scratch);
+  gci::MoeRouteCall call{experts, dest, routes, nranks, experts_per_rank, g.tile,
+                         reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base + g.counts_bytes),
+                         splits, stream};
+  return gci::launch_moe_route(call);
+}
+
+}  // namespace
+
 extern "C" gc_status gc_moe_route(const int32_t* const* experts, const int64_t* ntokens, int nranks, int topk,
                                   int experts_per_rank, int64_t* splits, int32_t* const* dest, void* scratch,
                                   size_t scratch_bytes, hipStream_t stream) {
   MoeRouteGeom g;
   GC_TRY(moe_route_geom(ntokens, nranks, topk, experts_per_rank, g));
-  const int N = nranks, E = experts_per_rank;
-  if (!experts || !dest || !splits || addr(splits) % 8) return GC_ERR_INVALID_ARG;
   if (!scratch || addr(scratch) % 256 || scratch_bytes < g.bytes) return GC_ERR_INVALID_ARG;
-  std::vector<Span> outs{span(splits, static_cast<uint64_t>(N) * N * E * 8), span(scratch, g.bytes)};
-  std::vector<Span> ins;
-  std::vector<int64_t> routes(N);
-  for (int s = 0; s < N; ++s) {
-    routes[s] = ntokens[s] * topk;
-    if (!routes[s]) continue;
-    if (!experts[s] || addr(experts[s]) % 4 || !dest[s] || addr(dest[s]) % 8) return GC_ERR_INVALID_ARG;
-    ins.push_back(span(experts[s], routes[s] * 4));
-    outs.push_back(span(dest[s], routes[s] * 8));
-  }
-  if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
-  for (const Span& o : outs)
-    for (const Span& i : ins)
-      if (overlaps(o, i)) return GC_ERR_INVALID_ARG;
-  char* base = static_cast<char*>(scratch);
-  gci::MoeRouteCall call{experts, dest, routes.data(), N, E, g.tile,
-                         reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base + g.counts_bytes),
-                         splits, stream};
-  return gci::launch_moe_route(call);
+  GC_TRY(moe_route_check(experts, ntokens, nranks, topk, experts_per_rank, splits, dest, span(scratch, g.bytes)));
+  return moe_route_launch(experts, ntokens, nranks, topk, experts_per_rank, splits, dest, scratch, g, stream);
+}
+
+extern "C" gc_status gc_moe_route_noalloc(const int32_t* const* experts, const int64_t* ntokens, int nranks,
+                                          int topk, int experts_per_rank, int64_t* splits, int32_t* const* dest,
+                                          hipStream_t stream) {
+  MoeRouteGeom g;
+  GC_TRY(moe_route_geom(ntokens, nranks, topk, experts_per_rank, g));
+  if (g.bytes > GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES) return GC_ERR_UNSUPPORTED;
+  GC_TRY(moe_route_check(experts, ntokens, nranks, topk, experts_per_rank, splits, dest, Span{0, 0}));
+  void* scratch = nullptr;
+  GC_TRY(gci::moe_route_static_scratch(stream, &scratch));
+  return moe_route_launch(experts, ntokens, nranks, topk, experts_per_rank, splits, dest, scratch, g, stream);
 }
 
 namespace {

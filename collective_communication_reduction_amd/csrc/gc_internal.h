@@ -144,6 +144,11 @@ struct MoeMoveCall {
 constexpr int32_t kMoeRouteTile = GC_MOE_ROUTE_TILE;
 
 gc_status launch_moe_route(const MoeRouteCall& call);
+
+// Device address of the routing plan's static scratch array on the device that
+// runs `stream` (the current device for the null stream), looked up once per
+// device; GC_ERR_HIP if the lookup fails.
+gc_status moe_route_static_scratch(hipStream_t stream, void** ptr);
 gc_status launch_moe_dispatch(const MoeMoveCall& call);
 gc_status launch_moe_combine(const MoeMoveCall& call);
 

@@ -19,6 +19,7 @@
 // skipped by dispatch and combine, so malformed plans cannot fault.
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "fold.h"
@@ -649,7 +650,47 @@ gc_status combine_any(const gci::MoeMoveCall& c) {
 
 }  // namespace
 
+// Scratch of the routing plan for gc_moe_route_noalloc: one copy per GPU the
+// library runs on, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it names a stand-in, not device
+// memory): the kernels get the per-device address hipGetSymbolAddress
+// returns, looked up once per device with that device current.
+static __device__ __align__(256) char scratch[GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
 namespace gci {
+
+gc_status moe_route_static_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return GC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return hip_status(e);
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256) return GC_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return GC_OK;
+}
 
 gc_status launch_moe_route(const MoeRouteCall& c) {
   return c.nranks <= 8 ? route_impl<8>(c) : route_impl<64>(c);

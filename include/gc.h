@@ -250,6 +250,28 @@ gc_status gc_moe_route(const int32_t* const* experts, const int64_t* ntokens, in
                        size_t scratch_bytes, hipStream_t stream);
 
 /*
+ * gc_moe_route for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as gc_moe_route, without the scratch buffer:
+ * the plan's scratch is a static array of GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES
+ * in the library, one per GPU, held until the process ends.  The call itself
+ * allocates nothing (no hipMalloc / hipFree, no host heap).  Plans that need
+ * more scratch than that (gc_moe_route_scratch_bytes()) are refused with
+ * GC_ERR_UNSUPPORTED before anything is launched; 4 MiB holds, for example,
+ * 8 ranks x 64 experts with up to 16,000 tiles of 1024 routes.  The array
+ * belongs to the device of `stream` (the current device for the null stream)
+ * and its address is looked up on the first call there (GC_ERR_HIP if that
+ * fails).  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (concurrent streams, or host threads) race and must be ordered by
+ * the caller.  Nothing has to be cleared between calls: every entry the plan
+ * reads was written earlier in the same call.
+ */
+#define GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+gc_status gc_moe_route_noalloc(const int32_t* const* experts, const int64_t* ntokens, int nranks, int topk,
+                               int experts_per_rank, int64_t* splits, int32_t* const* dest, hipStream_t stream);
+
+/*
  * Dispatch straight from token order: the pack by expert fused into the
  * all-to-all.  Row t of tokens[s] is read once and copied to recv[d] row r for
  * each of its routes (d, r) = dest[s][t * topk + k].  Equal to packing every

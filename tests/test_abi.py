@@ -223,6 +223,31 @@ def test_moe_route_validation():
     assert st(ntokens=[1 << 30, 1 << 30, 0]) == gc.GC_ERR_UNSUPPORTED       # 2^31 routes
 
 
+def test_moe_route_noalloc_validation():
+    # the variant without scratch: same checks, all made on the host before its scratch is looked up
+    route = gc.gc_moe_route_noalloc
+    nt = [100, 0, 37]
+    ex, de = _ptrs(3), _ptrs(3, base=FAKE + (1 << 40))
+    sp = FAKE + (1 << 41)
+    ok = dict(experts=ex, ntokens=nt, topk=2, experts_per_rank=4, splits=sp, dest=de, stream=0)
+
+    def st(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(route, **a)
+    big = [300_000] * 8                                                  # 38 MB of plan scratch
+    assert gc.gc_moe_route_scratch_bytes(big, 8, 64) > gc.GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES
+    assert st(experts=_ptrs(8), ntokens=big, topk=8, experts_per_rank=64,
+              dest=_ptrs(8, base=FAKE + (1 << 40))) == gc.GC_ERR_UNSUPPORTED
+    assert st(splits=sp + 4) == gc.GC_ERR_INVALID_ARG
+    assert st(dest=de[:2] + [de[2] + 4]) == gc.GC_ERR_INVALID_ARG
+    assert st(experts=[ex[0], ex[1], 0]) == gc.GC_ERR_INVALID_ARG
+    assert st(topk=0) == gc.GC_ERR_INVALID_ARG
+    assert st(topk=9) == gc.GC_ERR_UNSUPPORTED
+    assert st(splits=ex[2]) == gc.GC_ERR_INVALID_ARG
+    assert st(dest=[de[0], de[1], de[0] + 64]) == gc.GC_ERR_INVALID_ARG   # two dest tables overlap
+
+
 def test_moe_dispatch_combine_validation():
     nt, rows = [10, 0, 3], [8, 20, 0]
     tok, de = _ptrs(3), _ptrs(3, base=FAKE + (1 << 40))
