@@ -27,6 +27,14 @@ struct Span {
 
 Span span(const void* p, uint64_t bytes) { return Span{addr(p), addr(p) + bytes}; }
 
+// True if `bytes` bytes at p end inside the 64-bit address space.  Every
+// buffer extent a call derives is checked with it before any span is formed,
+// so spans never wrap and the addresses handed to the kernels never overflow.
+bool fits(const void* p, uint64_t bytes) { return bytes <= UINT64_MAX - addr(p); }
+
+// Address `off` bytes past p, computed on integers (the extent holding it was checked with fits).
+void* at(const void* p, uint64_t off) { return reinterpret_cast<void*>(addr(p) + off); }
+
 bool overlaps(const Span& a, const Span& b) { return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi; }
 
 // True if any two spans of `w` overlap.
@@ -51,10 +59,11 @@ gc_status check_ranks(int nranks) {
   return GC_OK;
 }
 
-gc_status check_ptrs(const void* const* p, int n, size_t es) {
+// n non-null pointers aligned to the element size, each holding `bytes` bytes.
+gc_status check_ptrs(const void* const* p, int n, size_t es, uint64_t bytes) {
   if (!p) return GC_ERR_INVALID_ARG;
   for (int i = 0; i < n; ++i)
-    if (!p[i] || addr(p[i]) % es) return GC_ERR_INVALID_ARG;
+    if (!p[i] || addr(p[i]) % es || !fits(p[i], bytes)) return GC_ERR_INVALID_ARG;
   return GC_OK;
 }
 
@@ -127,8 +136,8 @@ extern "C" gc_status gc_reduce_scatter(const void* const* send, void* const* rec
   if (mul_overflows(recv_count, N) || mul_overflows(recv_count * N, 4)) return GC_ERR_INVALID_ARG;
   if (recv_count == 0) return GC_OK;
   const size_t ei = elem_bytes(in_t), eo = elem_bytes(out_t);
-  GC_TRY(check_ptrs(send, nranks, ei));
-  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, eo));
+  GC_TRY(check_ptrs(send, nranks, ei, N * recv_count * ei));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, eo, recv_count * eo));
 
   // Aliasing: recv[r] may sit exactly on chunk r of send[r] when types match;
   // recv spans must not overlap each other nor any other part of any send.
@@ -160,8 +169,8 @@ extern "C" gc_status gc_all_gather(const void* const* send, void* const* recv, s
   if (mul_overflows(count, N) || mul_overflows(count * N, 4)) return GC_ERR_INVALID_ARG;
   if (count == 0) return GC_OK;
   const size_t es = elem_bytes(t);
-  GC_TRY(check_ptrs(send, nranks, es));
-  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es));
+  GC_TRY(check_ptrs(send, nranks, es, count * es));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es, N * count * es));
 
   // Aliasing: send[r] may sit exactly on slot r of recv[r]; otherwise no overlap.
   std::vector<Span> outs;
@@ -204,11 +213,11 @@ extern "C" gc_status gc_all_reduce(const void* const* send, void* const* recv, s
   if (mul_overflows(count, 4)) return GC_ERR_INVALID_ARG;
   if (count == 0) return GC_OK;
   const size_t es = elem_bytes(t);
-  GC_TRY(check_ptrs(send, nranks, es));
-  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es));
+  const uint64_t bytes = count * es;
+  GC_TRY(check_ptrs(send, nranks, es, bytes));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es, bytes));
 
   // Aliasing: each recv[r] is disjoint from every send[i] or equal to it.
-  const uint64_t bytes = count * es;
   std::vector<Span> outs;
   for (int r = 0; r < nranks; ++r) outs.push_back(span(recv[r], bytes));
   if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
@@ -223,7 +232,8 @@ extern "C" gc_status gc_all_reduce(const void* const* send, void* const* recv, s
     return gci::launch_all_reduce(call);
   }
 
-  if (!scratch || addr(scratch) % es || scratch_bytes < gc_all_reduce_scratch_bytes(count, nranks, t, algo))
+  if (!scratch || addr(scratch) % es || scratch_bytes < gc_all_reduce_scratch_bytes(count, nranks, t, algo) ||
+      !fits(scratch, scratch_bytes))
     return GC_ERR_INVALID_ARG;
   const Span sc = span(scratch, bytes);
   for (int r = 0; r < nranks; ++r)
@@ -235,7 +245,7 @@ extern "C" gc_status gc_all_reduce(const void* const* send, void* const* recv, s
   std::vector<const void*> shard_in(nranks);
   for (int j = 0; j < nranks; ++j) {
     const uint64_t lo = std::min<uint64_t>(count, static_cast<uint64_t>(j) * c);
-    shard_out[j] = static_cast<char*>(scratch) + lo * es;
+    shard_out[j] = at(scratch, lo * es);
     shard_in[j] = shard_out[j];
   }
   gci::ReduceCall rs{send, shard_out.data(), nranks, count, c, t, t, op == GC_AVG, order != GC_ORDER_RANK, stream};
@@ -276,6 +286,8 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
   std::vector<Span> all;
   for (int r = 0; r < N; ++r) {
     if ((send_rows[r] && !send[r]) || (recv_rows[r] && !recv[r])) return GC_ERR_INVALID_ARG;
+    if (!fits(send[r], send_rows[r] * row_bytes) || !fits(recv[r], recv_rows[r] * row_bytes))
+      return GC_ERR_INVALID_ARG;
     all.push_back(span(recv[r], recv_rows[r] * row_bytes));
   }
   if (any_overlap(all)) return GC_ERR_INVALID_ARG;
@@ -304,8 +316,8 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
         const size_t b = (static_cast<size_t>(s) * N + d) * E + e;
         const int64_t v = splits[b];
         if (v)
-          segs.push_back(gci::Segment{static_cast<const char*>(send[s]) + run * row_bytes,
-                                      static_cast<char*>(recv[d]) + roff[b] * row_bytes, v * row_bytes});
+          segs.push_back(gci::Segment{at(send[s], run * row_bytes), at(recv[d], roff[b] * row_bytes),
+                                      v * row_bytes});
         run += v;
       }
   }
@@ -332,10 +344,10 @@ extern "C" gc_status gc_hier_all_reduce(const void* const* send, void* const* re
   if (mul_overflows(count, 4)) return GC_ERR_INVALID_ARG;
   if (count == 0) return GC_OK;
   const size_t es = elem_bytes(t);
-  GC_TRY(check_ptrs(send, nranks, es));
-  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es));
-  // Aliasing as gc_all_reduce: each recv[r] is disjoint from every send[i] or equal to it.
   const uint64_t bytes = count * es;
+  GC_TRY(check_ptrs(send, nranks, es, bytes));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, es, bytes));
+  // Aliasing as gc_all_reduce: each recv[r] is disjoint from every send[i] or equal to it.
   std::vector<Span> outs;
   for (int r = 0; r < nranks; ++r) outs.push_back(span(recv[r], bytes));
   if (any_overlap(outs)) return GC_ERR_INVALID_ARG;
@@ -359,8 +371,8 @@ extern "C" gc_status gc_hsdp_reduce_scatter(const void* const* send, void* const
   if (mul_overflows(recv_count, S) || mul_overflows(recv_count * S, 4)) return GC_ERR_INVALID_ARG;
   if (recv_count == 0) return GC_OK;
   const size_t ei = elem_bytes(in_t), eo = elem_bytes(out_t);
-  GC_TRY(check_ptrs(send, nranks, ei));
-  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, eo));
+  GC_TRY(check_ptrs(send, nranks, ei, S * recv_count * ei));
+  GC_TRY(check_ptrs(const_cast<const void* const*>(recv), nranks, eo, recv_count * eo));
   // Aliasing: recv[r] may sit exactly on member i's chunk of send[r] (i = r mod
   // group) when the types match; no other overlap.
   std::vector<Span> outs;
@@ -446,8 +458,8 @@ gc_status fsdp2_check(const void* const* full, const void* const* part, const si
       const void* q = part[static_cast<size_t>(r) * P + p];
       const RowShard sh = row_shard(rows[p], N, r);
       const uint64_t n = (sh.hi - sh.lo) * cols[p];
-      if (!f || addr(f) % es_full) return GC_ERR_INVALID_ARG;
-      if (n && (!q || addr(q) % es_part)) return GC_ERR_INVALID_ARG;
+      if (!f || addr(f) % es_full || !fits(f, S * es_full)) return GC_ERR_INVALID_ARG;
+      if (n && (!q || addr(q) % es_part || !fits(q, n * es_part))) return GC_ERR_INVALID_ARG;
       const bool in_place = in_place_ok && n && addr(q) == addr(f) + sh.lo * cols[p] * es_full;
       const Tagged ft{span(f, S * es_full), p, r, in_place};
       const Tagged qt{span(n ? q : nullptr, n * es_part), p, r, in_place};
@@ -569,6 +581,7 @@ gc_status moe_route_check(const int32_t* const* experts, const int64_t* ntokens,
                           int experts_per_rank, const int64_t* splits, int32_t* const* dest, Span scratch) {
   const int N = nranks, E = experts_per_rank;
   if (!experts || !dest || !splits || addr(splits) % 8) return GC_ERR_INVALID_ARG;
+  if (!fits(splits, static_cast<uint64_t>(N) * N * E * 8)) return GC_ERR_INVALID_ARG;
   Span outs[GC_MAX_RANKS + 2], ins[GC_MAX_RANKS];
   int nout = 0, nin = 0;
   outs[nout++] = span(splits, static_cast<uint64_t>(N) * N * E * 8);
@@ -577,6 +590,7 @@ gc_status moe_route_check(const int32_t* const* experts, const int64_t* ntokens,
     const int64_t routes = ntokens[s] * topk;
     if (!routes) continue;
     if (!experts[s] || addr(experts[s]) % 4 || !dest[s] || addr(dest[s]) % 8) return GC_ERR_INVALID_ARG;
+    if (!fits(experts[s], routes * 4) || !fits(dest[s], routes * 8)) return GC_ERR_INVALID_ARG;
     ins[nin++] = span(experts[s], routes * 4);
     outs[nout++] = span(dest[s], routes * 8);
   }
@@ -608,7 +622,8 @@ extern "C" gc_status gc_moe_route(const int32_t* const* experts, const int64_t* 
                                   size_t scratch_bytes, hipStream_t stream) {
   MoeRouteGeom g;
   GC_TRY(moe_route_geom(ntokens, nranks, topk, experts_per_rank, g));
-  if (!scratch || addr(scratch) % 256 || scratch_bytes < g.bytes) return GC_ERR_INVALID_ARG;
+  if (!scratch || addr(scratch) % 256 || scratch_bytes < g.bytes || !fits(scratch, scratch_bytes))
+    return GC_ERR_INVALID_ARG;
   GC_TRY(moe_route_check(experts, ntokens, nranks, topk, experts_per_rank, splits, dest, span(scratch, g.bytes)));
   return moe_route_launch(experts, ntokens, nranks, topk, experts_per_rank, splits, dest, scratch, g, stream);
 }
@@ -648,13 +663,14 @@ gc_status moe_move_check(const void* const* src, const int64_t* src_rows, void* 
         mul_overflows(static_cast<uint64_t>(dst_rows[r]), row_bytes))
       return GC_ERR_INVALID_ARG;
     if ((src_rows[r] && !src[r]) || (dst_rows[r] && !dst[r])) return GC_ERR_INVALID_ARG;
+    if (!fits(src[r], src_rows[r] * row_bytes) || !fits(dst[r], dst_rows[r] * row_bytes)) return GC_ERR_INVALID_ARG;
     outs.push_back(span(dst[r], dst_rows[r] * row_bytes));
     ins.push_back(span(src[r], src_rows[r] * row_bytes));
     if (ntokens[r]) {
-      if (!dest[r] || addr(dest[r]) % 8) return GC_ERR_INVALID_ARG;
+      if (!dest[r] || addr(dest[r]) % 8 || !fits(dest[r], ntokens[r] * topk * 8)) return GC_ERR_INVALID_ARG;
       ins.push_back(span(dest[r], ntokens[r] * topk * 8));
       if (weights) {
-        if (!weights[r] || addr(weights[r]) % 4) return GC_ERR_INVALID_ARG;
+        if (!weights[r] || addr(weights[r]) % 4 || !fits(weights[r], ntokens[r] * topk * 4)) return GC_ERR_INVALID_ARG;
         ins.push_back(span(weights[r], ntokens[r] * topk * 4));
       }
     }
@@ -790,21 +806,22 @@ gc_status bucket_segments(const gc_bucket_plan* p, int bucket, const void* const
   std::vector<Span> writes, reads;
   for (int r = 0; r < nranks; ++r) {
     const void* buf_r = packing ? static_cast<const void*>(bufs_out[r]) : bufs_in[r];
-    if (p->padded[bucket] && (!buf_r || addr(buf_r) % es)) return GC_ERR_INVALID_ARG;
+    if (p->padded[bucket] && (!buf_r || addr(buf_r) % es || !fits(buf_r, p->padded[bucket] * es)))
+      return GC_ERR_INVALID_ARG;
     const Span bspan = span(buf_r, p->padded[bucket] * es);
     (packing ? writes : reads).push_back(bspan);
     for (int ti : b) {
       const size_t n = p->numel[ti];
       if (!n) continue;
       const void* tp = packing ? tensors[r * T + ti] : static_cast<const void*>(tensor_out[r * T + ti]);
-      if (!tp || addr(tp) % es) return GC_ERR_INVALID_ARG;
+      if (!tp || addr(tp) % es || !fits(tp, n * es)) return GC_ERR_INVALID_ARG;
       (packing ? reads : writes).push_back(span(tp, n * es));
-      char* bb = static_cast<char*>(const_cast<void*>(buf_r)) + p->tensor_offset[ti] * es;
+      void* bb = at(buf_r, p->tensor_offset[ti] * es);
       if (packing) segs->push_back(gci::Segment{tp, bb, n * es});
       else segs->push_back(gci::Segment{bb, const_cast<void*>(tp), n * es});
     }
     if (packing && p->padded[bucket] > p->used[bucket])
-      segs->push_back(gci::Segment{nullptr, static_cast<char*>(bufs_out[r]) + p->used[bucket] * es,
+      segs->push_back(gci::Segment{nullptr, at(bufs_out[r], p->used[bucket] * es),
                                    (p->padded[bucket] - p->used[bucket]) * es});
   }
   if (any_overlap(writes)) return GC_ERR_INVALID_ARG;
@@ -823,7 +840,7 @@ extern "C" gc_status gc_bucket_all_reduce(const gc_bucket_plan* p, int bucket, v
       !valid_order(order))
     return GC_ERR_INVALID_ARG;
   if (p->t == GC_INT32 && (op == GC_AVG || sumsq)) return GC_ERR_UNSUPPORTED;
-  if (sumsq && addr(sumsq) % 8) return GC_ERR_INVALID_ARG;
+  if (sumsq && (addr(sumsq) % 8 || !fits(sumsq, 8))) return GC_ERR_INVALID_ARG;
   const size_t T = p->numel.size();
   const size_t es = p->es;
   const std::vector<int>& b = p->buckets[bucket];
@@ -839,7 +856,7 @@ extern "C" gc_status gc_bucket_all_reduce(const gc_bucket_plan* p, int bucket, v
     if (!n) continue;
     for (int r = 0; r < nranks; ++r) {
       void* tp = tensors[static_cast<size_t>(r) * T + ti];
-      if (!tp || addr(tp) % es) return GC_ERR_INVALID_ARG;
+      if (!tp || addr(tp) % es || !fits(tp, n * es)) return GC_ERR_INVALID_ARG;
       spans.push_back(span(tp, n * es));
       slot_ptrs.push_back(tp);
     }
