@@ -77,6 +77,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-copy-ceiling", action="store_true", help="skip the 2 GiB copy-ceiling measurement")
+    p.add_argument("--no-extras", action="store_true",
+                   help="the default workload only: skip the other configurations' extra keys")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="also launch a plain device copy of this many MiB (counter calibration runs)")
     return p.parse_args()
@@ -113,6 +115,7 @@ class Workload:
     bytes_per_step = 0
     dominant = ""
     dominant_bytes = 0
+    dtype = "f32"          # the arithmetic type of the step (fp32 accumulation); movement-only steps override
 
     def step(self, k):
         raise NotImplementedError
@@ -169,7 +172,7 @@ class AllReduceWorkload(Workload):
         import collective_communication_reduction_amd as gc
         from gen import device as GD
         self.gc = gc
-        self.N, self.S, self.dtype, self.op = nranks, count, dtype, op
+        self.N, self.S, self.dtype_storage, self.op = nranks, count, dtype, op
         tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
         es = 2 if dtype == "bf16" else 4
         self.algo = args.algo
@@ -204,13 +207,14 @@ class AllReduceWorkload(Workload):
         self.stream = torch.cuda.current_stream().cuda_stream
         torch.cuda.synchronize()
 
-    def step(self, k):
+    def step(self, k, stream=None):
         sp, rp = self.ptrs[k % len(self.ptrs)]
         self.gc.gc_all_reduce(sp, rp, op=self.op, order=self.order, algo=self.algo, scratch=self.scratch,
-                              count=self.S, dtype=self.dtype, stream=self.stream)
+                              count=self.S, dtype=self.dtype_storage,
+                              stream=self.stream if stream is None else stream)
 
     def config(self):
-        return {"workload": self.name, "nranks": self.N, "count_per_rank": self.S, "storage": self.dtype,
+        return {"workload": self.name, "nranks": self.N, "count_per_rank": self.S, "storage": self.dtype_storage,
                 "op": self.op, "order": self.order, "algo": self.algo, "replicas": len(self.sets), "layout": self.layout}
 
     def cpu_sample(self, seed):
@@ -222,11 +226,11 @@ class AllReduceWorkload(Workload):
         xs = []
         for r in range(self.N):
             key = _keyed(seed, r)
-            xs.append(G.normal_bf16(key, np.arange(S), 1e-3) if self.dtype == "bf16" else
+            xs.append(G.normal_bf16(key, np.arange(S), 1e-3) if self.dtype_storage == "bf16" else
                       G.uniform_f32(key, np.arange(S)))
-        es = 2 if self.dtype == "bf16" else 4
-        return (lambda: C.all_reduce(xs, self.dtype, self.op, "ring"), 2 * self.N * S * es,
-                f"oracle ring all-reduce of {self.N} ranks x {S} {self.dtype} (first quarter of each buffer)")
+        es = 2 if self.dtype_storage == "bf16" else 4
+        return (lambda: C.all_reduce(xs, self.dtype_storage, self.op, "ring"), 2 * self.N * S * es,
+                f"oracle ring all-reduce of {self.N} ranks x {S} {self.dtype_storage} (first quarter of each buffer)")
 
 
 class DdpWorkload(Workload):
@@ -293,10 +297,12 @@ class DdpWorkload(Workload):
                 marks[b][1].record()
             plan.unpack(b, views, self.tensor_ptrs, N)
 
-    def dominant_in_step(self, steps):
+    def allreduce_in_step(self, steps):
         """ms per step inside the all-reduce launches, each bracketed by events within
         whole steps, so that every bucket is read right after its pack as in the timed
-        steps (None for the zero-copy step, whose launches are the whole step)."""
+        steps (None for the zero-copy step, whose launches are the whole step).  Part of
+        each freshly packed bucket is then served by the 256 MB MALL, so bytes over this
+        time are algorithmic bytes, not HBM bytes."""
         import torch
         if self.zero_copy:
             return None
@@ -637,6 +643,7 @@ class MoeWorkload(Workload):
         self.dominant_bytes = self.bytes_per_step
         self.frac_dst0 = float(self.splits[:, 0, :].sum() / total_rows)
         self.rows = rows
+        self.dtype = "bf16"   # pure movement of bf16 rows
         torch.cuda.synchronize()
 
     def step(self, k):
@@ -870,6 +877,138 @@ def _quantile(xs, q):
     return ys[lo] + (ys[hi] - ys[lo]) * (k - lo)
 
 
+def measure(w, steps, warmup):
+    """The step time (K steps back to back), the per-step spread (the same K steps,
+    each bracketed by its own events: for a few-microsecond step those records are
+    host work the GPU would wait for, so they stay out of the first pass), and the
+    dominant kernel's time per step: the whole step where it is one launch, else
+    its launches alone."""
+    ms = time_steps(w.step, steps, warmup)
+    step_ms = []
+    time_steps(w.step, steps, 0, step_ms)
+    kms = ms if type(w).dominant_launch is Workload.dominant_launch else \
+        time_steps(w.dominant_launch, max(3, steps // 5), 2)
+    return ms, step_ms, kms
+
+
+def roofline(w, kms):
+    achieved = w.dominant_bytes / (kms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(w.name),
+            "kernel": w.dominant, "algorithmic_bytes_per_launch": w.dominant_bytes}
+
+
+def graph_us(launch, n):
+    """GPU time per launch of `launch(k, stream)` for k < n, captured into one HIP
+    graph and replayed (no host work between launches: the device-side cost of
+    each launch)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for k in range(n):                 # warm the code path on a side stream
+            launch(k, s.cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for k in range(n):
+            launch(k, cs)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    reps = 20
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e3 / (reps * n)
+
+
+def launch_floor(w):
+    """The all-reduce call path at its smallest: the same ranks and type, 4 elements
+    per rank (one element per owner chunk, N workgroups), back to back eagerly and
+    in a HIP graph.  The difference between a workload's time and this floor is
+    what its bytes cost beyond launching."""
+    import torch
+    gc = w.gc
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[w.dtype_storage]
+    send = [torch.ones(4, dtype=tdt, device="cuda") for _ in range(w.N)]
+    recv = [torch.empty(4, dtype=tdt, device="cuda") for _ in range(w.N)]
+    sp, rp = gc.gc_pointers(send), gc.gc_pointers(recv)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def one(_k, st):
+        gc.gc_all_reduce(sp, rp, op=w.op, order="ring", count=4, dtype=w.dtype_storage, stream=st)
+    eager = time_steps(lambda k: one(k, stream), 200, 20) * 1e3
+    return {"eager_us": round(eager, 3), "graph_us": round(graph_us(one, 100), 3),
+            "what": f"all-reduce of 4 elements per rank ({w.N} ranks, {w.dtype_storage}, {w.N} workgroups)"}
+
+
+def extra_line(w, steps, warmup):
+    """ms per step, value and roofline of one more workload, for the default run's extra keys."""
+    ms, step_ms, kms = measure(w, steps, warmup)
+    out = {"ms_per_step": round(ms, 5), "value": round(w.bytes_per_step / (ms * 1e-3) / 1e9, 2),
+           "unit": "GB/s (algorithmic bytes per step / step time)", "dtype": w.dtype, "steps": steps,
+           "warmup": warmup, "bytes_per_step": w.bytes_per_step,
+           "step_ms": {"median": round(_quantile(step_ms, 0.5), 5), "min": round(min(step_ms), 5),
+                       "p90": round(_quantile(step_ms, 0.9), 5)},
+           "roofline": roofline(w, kms), "config": w.config()}
+    return out
+
+
+EXTRAS = (
+    # (key, workload, layout, steps, warmup)
+    ("ar_bf16_n8_separate", "ar_bf16_n8", "separate", 20, 5),
+    ("ar_fp32_n4", "ar_fp32_n4", "arena", 50, 10),
+    ("fsdp_layer_n64", "fsdp_layer_n64", "arena", 10, 3),
+    ("moe_a2a_n8", "moe_a2a_n8", "arena", 20, 5),
+    ("ddp_llama7b", "ddp_llama7b", "arena", 3, 1),
+)
+
+
+def run_extras(args):
+    """The remaining configurations of the target, measured one after another in
+    this process (each one's memory released before the next is built)."""
+    import gc as pygc
+    import torch
+    out = {}
+    for key, name, layout, steps, warmup in EXTRAS:
+        a = argparse.Namespace(**vars(args))
+        a.workload, a.layout, a.algo, a.order, a.stagger = name, layout, "fused", "ring", None
+        w = make(a)
+        line = extra_line(w, steps, warmup)
+        if name == "ar_fp32_n4":
+            # A 7-microsecond step is shorter than one pass of the Python loop that issues it, so the
+            # eager steps measure the host.  In a HIP graph (one replay = 128 launches over the 32
+            # replica sets) the launches run back to back on the device: that is the kernel's time.
+            floor = launch_floor(w)
+            n = len(w.ptrs)
+            g_us = graph_us(w.step, 4 * n)
+            line["graph"] = {"us_per_step": round(g_us, 3), "value": round(w.bytes_per_step / (g_us * 1e-6) / 1e9, 2),
+                             "launches_per_replay": 4 * n}
+            line["roofline"] = roofline(w, g_us * 1e-3)
+            line["roofline"]["note"] = "per-launch time in a HIP graph (the eager steps are bound by the host loop)"
+            line["launch_floor"] = floor
+            line["over_floor_us"] = round(g_us - floor["graph_us"], 3)
+        if name == "ddp_llama7b":
+            ar = w.allreduce_in_step(steps)
+            line["allreduce_in_step"] = {
+                "ms_per_step": round(ar, 4), "value": round(w.dominant_bytes / (ar * 1e-3) / 1e9, 2),
+                "unit": "GB/s (algorithmic: part of each freshly packed bucket is served by the 256 MB MALL)"}
+            line["roofline"]["note"] = "the 226 bucket all-reduces launched alone (no pack before them): HBM-bound"
+        out[key] = line
+        del w
+        pygc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -887,23 +1026,11 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
     # The measurement: K steps back to back, nothing else inside the timed region.
-    ms = time_steps(w.step, args.steps, args.warmup)
-    # The spread: the same K steps again, each bracketed by its own events (an event
-    # record per step is host work a few-microsecond step would feel in the first pass).
-    step_ms = []
-    time_steps(w.step, args.steps, 0, step_ms)
-    # The dominant kernel's time per step: timed inside whole steps where a workload can
-    # bracket its launches with events, else the whole step (one launch), else its
-    # launches alone.
-    kms = w.dominant_in_step(max(3, args.steps // 5)) if hasattr(w, "dominant_in_step") else None
-    if kms is None:
-        kms = ms if type(w).dominant_launch is Workload.dominant_launch else \
-            time_steps(w.dominant_launch, max(3, args.steps // 5), 2)
+    ms, step_ms, kms = measure(w, args.steps, args.warmup)
     value = w.bytes_per_step / (ms * 1e-3) / 1e9
-    achieved = w.dominant_bytes / (kms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(w.name)
     out = {
-        "metric": METRIC if w.name == "ar_bf16_n8" else f"effective HBM GB/s for {w.name} on 1 MI355X",
+        "metric": METRIC if w.name == "ar_bf16_n8" else
+        f"algorithmic GB/s (bytes the step must move / step time) for {w.name} on 1 MI355X",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -913,25 +1040,36 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": w.config(),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": w.dominant, "algorithmic_bytes_per_launch": w.dominant_bytes},
+        "roofline": roofline(w, kms),
         "bytes_per_step": w.bytes_per_step,
         "step_ms": {"median": round(_quantile(step_ms, 0.5), 5), "min": round(min(step_ms), 5),
                     "p90": round(_quantile(step_ms, 0.9), 5)},
     }
+    if hasattr(w, "allreduce_in_step"):
+        ar = w.allreduce_in_step(max(3, args.steps // 5))
+        if ar is not None:
+            out["allreduce_in_step"] = {
+                "ms_per_step": round(ar, 4), "value": round(w.dominant_bytes / (ar * 1e-3) / 1e9, 2),
+                "unit": "GB/s (algorithmic: part of each freshly packed bucket is served by the 256 MB MALL)"}
     if not args.no_copy_ceiling:
         ceiling = copy_ceiling()
         out["copy_ceiling"] = {"value": round(ceiling, 2), "unit": "GB/s",
                                "kernel": "segment_vec_kernel, one 2 GiB block (16-byte loads, 16-byte device-scope stores)",
-                               "frac": round(achieved / ceiling, 4)}
+                               "frac": round(out["roofline"]["achieved"] / ceiling, 4)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.seed)
     else:
         out["cpu_baseline"] = None
+    if not args.no_extras and args.workload == "ar_bf16_n8":
+        del w
+        import gc as pygc
+        pygc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out.update(run_extras(args))
     print(json.dumps(out), flush=True)
 
 
