@@ -74,6 +74,8 @@ def parse():
                    help="extra bytes between consecutive ranks' memory (default: the workload's, else 4096)")
     p.add_argument("--max-region", type=int, default=32, metavar="GIB",
                    help="largest per-rank region of the rank arena (a power of two, GiB)")
+    p.add_argument("--region-bytes", type=int, default=None, metavar="BYTES",
+                   help="exact per-rank region of the rank arena (ranks are region + stagger bytes apart)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-copy-ceiling", action="store_true", help="skip the 2 GiB copy-ceiling measurement")
@@ -142,7 +144,8 @@ class Layout:
         self.kind = args.layout
         self.nranks = nranks
         self.stagger = args.stagger if args.stagger is not None else (stagger or 4096)
-        self.arena = (gc.RankArena(nranks, stagger_bytes=self.stagger, max_region=args.max_region << 30)
+        self.arena = (gc.RankArena(nranks, region_bytes=getattr(args, "region_bytes", None), stagger_bytes=self.stagger,
+                                   max_region=args.max_region << 30)
                       if self.kind == "arena" else None)
 
     def buffers(self, count, tdt):
@@ -158,7 +161,9 @@ class Layout:
             return "separate allocations"
         if self.kind == "staggered":
             return f"one allocation per buffer set, {self.stagger} B per-rank stagger"
-        return f"rank arena: {self.arena.region >> 30} GiB region per rank, {self.stagger} B stagger"
+        reg = self.arena.region
+        size = f"{reg >> 30} GiB" if reg % (1 << 30) == 0 else f"{reg} B"
+        return f"rank arena: {size} region per rank, {self.stagger} B stagger"
 
 
 def _keyed(seed, r, stream=0):
