@@ -950,8 +950,11 @@ def launch_floor(w):
     def one(_k, st):
         gc.gc_all_reduce(sp, rp, op=w.op, order="ring", count=4, dtype=w.dtype_storage, stream=st)
     eager = time_steps(lambda k: one(k, stream), 200, 20) * 1e3
+    empty = graph_us(lambda _k, _st: torch.cuda._sleep(0), 100)   # a kernel that does nothing
     return {"eager_us": round(eager, 3), "graph_us": round(graph_us(one, 100), 3),
-            "what": f"all-reduce of 4 elements per rank ({w.N} ranks, {w.dtype_storage}, {w.N} workgroups)"}
+            "empty_kernel_graph_us": round(empty, 3),
+            "what": f"all-reduce of 4 elements per rank ({w.N} ranks, {w.dtype_storage}, {w.N} workgroups); "
+                    "empty kernel: torch.cuda._sleep(0)"}
 
 
 def extra_line(w, steps, warmup):
