@@ -3,6 +3,8 @@
 // before anything is enqueued, so a non-OK status means no work was launched.
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <new>
 #include <vector>
 
@@ -92,6 +94,45 @@ constexpr gci::StorePolicy kUnpackStore = GC_UNPACK_STORE;
     const gc_status _s = (expr);        \
     if (_s != GC_OK) return _s;         \
   } while (0)
+
+// ------------------------------------------------------------ GC_DEBUG checks
+// With GC_DEBUG set to a value other than "0" in the environment, every launch
+// first checks the tables the host planners built for it: copy segments write
+// disjoint ranges and none of them reads what another writes; a bucket's
+// pieces cover each tensor exactly once, in owner-chunk order, with a valid
+// fold start.  These are invariants of the library's own planning (arguments
+// were validated before), so a failure is a library bug: it is reported on
+// stderr and the call returns GC_ERR_INVALID_ARG with nothing launched.
+
+bool debug_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("GC_DEBUG");
+    return v && *v && !(v[0] == '0' && v[1] == 0);
+  }();
+  return on;
+}
+
+gc_status debug_fail(const char* what) {
+  std::fprintf(stderr, "libgc GC_DEBUG: %s\n", what);
+  return GC_ERR_INVALID_ARG;
+}
+
+gc_status debug_segments(const gci::Segment* segs, size_t n) {
+  if (!debug_on()) return GC_OK;
+  std::vector<Span> dst, src;
+  for (size_t i = 0; i < n; ++i) {
+    if (!segs[i].bytes || !segs[i].dst) return debug_fail("empty or null copy segment");
+    if (!fits(segs[i].dst, segs[i].bytes) || (segs[i].src && !fits(segs[i].src, segs[i].bytes)))
+      return debug_fail("copy segment wraps the address space");
+    dst.push_back(span(segs[i].dst, segs[i].bytes));
+    if (segs[i].src) src.push_back(span(segs[i].src, segs[i].bytes));
+  }
+  if (any_overlap(dst)) return debug_fail("two copy segments write overlapping ranges");
+  for (const Span& d : dst)
+    for (const Span& r : src)
+      if (overlaps(d, r)) return debug_fail("a copy segment writes what another reads");
+  return GC_OK;
+}
 
 }  // namespace
 
@@ -321,6 +362,7 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
         run += v;
       }
   }
+  GC_TRY(debug_segments(segs.data(), segs.size()));
   return gci::launch_segment_copy(segs.data(), segs.size(), kA2aStore, stream);
 }
 
@@ -877,6 +919,28 @@ extern "C" gc_status gc_bucket_all_reduce(const gc_bucket_plan* p, int bucket, v
     for (const Span& t : spans)
       if (overlaps(sq, t)) return GC_ERR_INVALID_ARG;
   }
+  if (debug_on()) {
+    // pieces of each slot: consecutive, starting at 0, ending at the tensor's length, each inside one owner
+    // chunk of the packed bucket and folded from that chunk's first rank
+    size_t k = 0;
+    uint32_t sl = 0;
+    for (int ti : b) {
+      const uint64_t n = p->numel[ti];
+      if (!n) continue;
+      uint64_t at_ = 0;
+      for (; k < pieces.size() && pieces[k].slot == sl; ++k) {
+        const gci::BucketPiece& pc = pieces[k];
+        const uint64_t g0 = p->tensor_offset[ti] + pc.lo;
+        if (pc.lo != at_ || !pc.len || g0 / c != (g0 + pc.len - 1) / c ||
+            (order != GC_ORDER_RANK && pc.first != (g0 / c + 1) % nranks) || pc.first >= static_cast<uint32_t>(nranks))
+          return debug_fail("bucket pieces do not tile a tensor by owner chunks");
+        at_ += pc.len;
+      }
+      if (at_ != n) return debug_fail("bucket pieces do not cover a tensor");
+      ++sl;
+    }
+    if (k != pieces.size()) return debug_fail("bucket piece outside every tensor");
+  }
   gci::BucketCall call{slot_ptrs.data(), static_cast<int>(slot), nranks, pieces.data(),
                        static_cast<int>(pieces.size()), p->t, op == GC_AVG, sumsq, stream};
   call.wire = order == GC_ORDER_RING_WIRE;
@@ -888,6 +952,7 @@ extern "C" gc_status gc_bucket_pack(const gc_bucket_plan* p, int bucket, const v
   if (!tensors || !bucket_bufs) return GC_ERR_INVALID_ARG;
   std::vector<gci::Segment> segs;
   GC_TRY(bucket_segments(p, bucket, tensors, nullptr, nullptr, bucket_bufs, nranks, true, &segs));
+  GC_TRY(debug_segments(segs.data(), segs.size()));
   return gci::launch_segment_copy(segs.data(), segs.size(), kPackStore, stream);
 }
 
@@ -896,5 +961,6 @@ extern "C" gc_status gc_bucket_unpack(const gc_bucket_plan* p, int bucket, const
   if (!tensors || !bucket_bufs) return GC_ERR_INVALID_ARG;
   std::vector<gci::Segment> segs;
   GC_TRY(bucket_segments(p, bucket, nullptr, tensors, bucket_bufs, nullptr, nranks, false, &segs));
+  GC_TRY(debug_segments(segs.data(), segs.size()));
   return gci::launch_segment_copy(segs.data(), segs.size(), kUnpackStore, stream);
 }

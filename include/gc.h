@@ -46,9 +46,16 @@
  * communication, fp32 arithmetic): every partial a rank forwards is rounded to
  * the input type (bf16: nearest, ties to even) before the next rank adds its
  * own term in fp32; the owner's last add and the epilogue are as above.  For
- * fp32 and int32 inputs it equals GC_ORDER_RING.  Accepted by gc_all_reduce,
- * gc_reduce_scatter and gc_fsdp2_reduce_scatter; gc_bucket_all_reduce
- * returns GC_ERR_UNSUPPORTED for it on bf16 buckets.
+ * fp32 and int32 inputs it equals GC_ORDER_RING.  Every reduction accepts it;
+ * in the two-level calls both levels forward bf16 partials (inside a group
+ * before the next member adds its term, across groups before the next group
+ * adds its own partial).
+ *
+ * Debug checks.  With GC_DEBUG set to a value other than "0" in the
+ * environment (read once), each call also checks the launch tables the host
+ * planned from its arguments (copy segments write disjoint ranges that no other
+ * segment reads; bucket pieces tile every tensor by owner chunk) and refuses
+ * the call with GC_ERR_INVALID_ARG and a message on stderr if one fails.
  */
 #ifndef GC_H
 #define GC_H

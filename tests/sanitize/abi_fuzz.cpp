@@ -11,6 +11,7 @@
 //   * the status is one of the gc_status values;
 //   * a non-OK status launched nothing (validation precedes every launch);
 //   * every launch stays inside the declared buffers (checked by the stubs);
+//   * the library's GC_DEBUG checks of its own plan tables never fire;
 // and over the run, every entry point returned GC_OK at least once and was
 // refused at least once.  Exit status 0 means all held; the sanitizers abort
 // the run on their first report.
@@ -398,6 +399,8 @@ void fuzz_buckets(uint64_t it) {
 }  // namespace
 
 int main(int argc, char** argv) {
+  // the library's own plan-table checks run before every launch (a failure is printed and refuses the call)
+  setenv("GC_DEBUG", "1", 1);
   const uint64_t iters = argc > 1 ? std::strtoull(argv[1], nullptr, 10) : 20000;
   const uint64_t seed = argc > 2 ? std::strtoull(argv[2], nullptr, 10) : 1;
   g_rng.seed(seed);

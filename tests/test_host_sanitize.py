@@ -1,9 +1,10 @@
 """The C ABI's host layer (argument validation, aliasing rules, chunk / bucket /
 all-to-all / routing planning in api.cpp) built for the host with
 AddressSanitizer and UndefinedBehaviorSanitizer, linked against launch stubs,
-and driven by a seeded argument fuzz (tests/sanitize/abi_fuzz.cpp): no
-sanitizer report, no launch after a refused call, every launch inside the
-buffers the contract gives the caller, and every entry point both accepted and
+and driven by a seeded argument fuzz (tests/sanitize/abi_fuzz.cpp) with the
+library's GC_DEBUG plan-table checks switched on: no sanitizer report, no
+launch after a refused call, every launch inside the buffers the contract gives
+the caller, no plan-table check firing, and every entry point both accepted and
 refused some calls.  No GPU is involved."""
 
 import os
@@ -33,4 +34,5 @@ def test_abi_fuzz_under_asan_and_ubsan(fuzzer, seed):
     p = subprocess.run([fuzzer, "30000", str(seed)], capture_output=True, text=True, timeout=600, env=env)
     assert p.returncode == 0, (p.stdout[-2000:], p.stderr[-4000:])
     assert "runtime error" not in p.stderr and "AddressSanitizer" not in p.stderr, p.stderr[-4000:]
+    assert "GC_DEBUG" not in p.stderr, p.stderr[-4000:]        # the library's plan-table checks held
     assert ", 0 failures" in p.stdout, p.stdout[-2000:]
