@@ -169,9 +169,10 @@ gc_status gc_all_to_all(const void* const* send, void* const* recv, const int64_
  * pieces of ceil(len_i / R); piece h folded from group h+1 around to group h),
  * then an all-gather inside each group.  The epilogue runs once at the end
  * (GC_AVG divides by nranks).  GC_ORDER_RANK folds members 0.. and groups 0..
- * instead.  GC_ORDER_RING_WIRE is GC_ERR_UNSUPPORTED for bf16 (for fp32 and
- * int32 it is the ring).  One pass: every input is read once and every output
- * written once.  Types and aliasing as gc_all_reduce.
+ * instead.  GC_ORDER_RING_WIRE is the same schedule with every forwarded
+ * partial rounded to bf16 at both levels (for fp32 and int32 it is the ring).
+ * One pass: every input is read once and every output written once.  Types
+ * and aliasing as gc_all_reduce.
  */
 gc_status gc_hier_all_reduce(const void* const* send, void* const* recv, size_t count, int nranks, int group_size,
                              gc_dtype t, gc_op op, gc_order order, hipStream_t stream);
