@@ -66,6 +66,17 @@ __device__ __forceinline__ void st16p(void* p, u32x4 v) {
   }
 }
 
+// Vector u (0..U-1) of this thread within a tile of kThreads * U vectors that
+// starts at vector tv0.  WAVE = true: each wavefront covers its U * 64 vectors
+// contiguously (a wavefront's U load instructions per rank read one run of
+// U KiB); false: the workgroup covers kThreads consecutive vectors per u (each
+// instruction reads 1 KiB, the U of them kThreads * 16 bytes apart).
+template <int U, bool WAVE>
+__device__ __forceinline__ uint64_t tile_vec(uint64_t tv0, int u) {
+  if constexpr (WAVE) return tv0 + (threadIdx.x >> 6) * (64 * U) + u * 64 + (threadIdx.x & 63);
+  else return tv0 + u * kThreads + threadIdx.x;
+}
+
 // ---------------------------------------------------------------- inputs
 // In::VE elements fill one 16-byte vector; In::Acc is the reduction type
 // (fp32 for bf16 / fp32 data, uint32 with wrap-around for int32 data).
