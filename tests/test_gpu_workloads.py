@@ -119,6 +119,33 @@ def _llama_layout():
     return numels, offs
 
 
+# one bucket of every composition the 226-bucket plan has: lm_head alone; final norm + layer 31's norms and
+# down_proj; then a layer's up, gate, o, v, k, q and [norms, down_proj] (each repeated 31-32 times); embedding
+FULL_BUCKETS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 225)
+
+
+def _ddp_bucket_full(result, b, ts, numels, offs, keys, sigma, N):
+    """Every output of bucket b against the oracle's all-reduce of the packed bucket.  The inputs (consumed
+    in place by the step) are regenerated by index with the device generator, which is pinned bit for bit to
+    the host one, and packed on the host in the bucket's order."""
+    boffs, used, _ = OB.bucket_layout(ts, numels)
+    tmp = torch.empty(max(numels[t] for t in ts), dtype=torch.bfloat16, device=DEV)
+    packed = np.empty((N, used), dtype=np.uint16)
+    for r in range(N):
+        for t, o in zip(ts, boffs):
+            GD.fill_normal_bf16(tmp[:numels[t]], keys[r], sigma, base=int(offs[t]))
+            packed[r, o:o + numels[t]] = from_dev(tmp[:numels[t]])
+    got = np.empty(used, dtype=np.uint16)
+    for t, o in zip(ts, boffs):
+        got[o:o + numels[t]] = from_dev(result[t])
+    c = -(-used // N)
+    for j in range(N):
+        lo, hi = min(used, j * c), min(used, (j + 1) * c)
+        if lo < hi:
+            want = SM.reduce_scatter_owner([packed[r, lo:hi] for r in range(N)], j, "bf16", "bf16", "avg", "ring")
+            assert_same(got[lo:hi], want, "bf16", f"bucket {b} owner chunk {j}")
+
+
 def test_ddp_llama7b_full_step():
     cfg = WORKLOADS["ddp_llama7b"]
     N, sigma, cap = cfg["nranks"], cfg["sigma"], cfg["cap_bytes"]
@@ -160,6 +187,9 @@ def test_ddp_llama7b_full_step():
     got = _gather(flat[5], flat_pos)
     assert max_ulp(got, want) <= 1
     assert_same(got, want, "bf16", "sampled bucket outputs")
+    T = len(numels)
+    for b in FULL_BUCKETS:                              # every output of one bucket of each composition
+        _ddp_bucket_full(tensors[5 * T:6 * T], b, oracle_buckets[b], numels, offs, keys, sigma, N)
     plan.close()
 
 
@@ -198,6 +228,9 @@ def test_ddp_llama7b_zero_copy_full_step():
         flat_pos.append(fidx)
     got = _gather(flat[2], np.concatenate(flat_pos))
     assert_same(got, np.concatenate(want), "bf16", "sampled zero-copy outputs")
+    T = len(numels)
+    for b in FULL_BUCKETS:                              # every output of one bucket of each composition
+        _ddp_bucket_full(tensors[2 * T:3 * T], b, oracle_buckets[b], numels, offs, keys, sigma, N)
     # the accumulated sum of squares equals the squared norm of the synced gradients (any order: fp64
     # relative bound over 6.7e9 terms)
     norm2 = 0.0
