@@ -321,7 +321,9 @@ def test_moe_ep_n8_full():
     """Routing plan, dispatch and combine at full size, in bench.py's layout.
     The plan is compared with the oracle's for all 262,144 routes; dispatched
     and combined rows are sampled against values the oracle computes from the
-    host generator (identity experts: a token's K expert rows are its own row)."""
+    host generator (identity experts: a token's K expert rows are its own row),
+    then every dispatched row against the token row its route names and every
+    combined row against the oracle's weighted sum of the token's rows."""
     from gen.workloads import route_tokens
     from oracle import moe as OM
     cfg = WORKLOADS["moe_ep_n8"]
@@ -370,6 +372,23 @@ def test_moe_ep_n8_full():
         want = OM.combine_rows(np.stack([tok_rows] * K), w, "bf16")
         got = from_dev(out[s].view(-1, H).index_select(0, torch.from_numpy(pick).to(DEV)))
         assert_same(got.reshape(-1), want.reshape(-1), "bf16", f"source {s} combine")
+    # every dispatched row is the token row its route names (pure movement, compared on the device) ...
+    all_tok = torch.cat([t.view(-1, H) for t in tokens])
+    for d in range(N):
+        idx = np.full(rows[d], -1, dtype=np.int64)
+        for s in range(N):
+            m = dr[s] == d
+            idx[dw[s][m]] = s * T + np.arange(T * K)[m] // K
+        assert (idx >= 0).all()
+        want = all_tok.index_select(0, torch.from_numpy(idx).to(DEV))
+        assert torch.equal(recv[d].view(-1, H).view(torch.int16), want.view(torch.int16)), f"dispatch rank {d}"
+    del all_tok
+    # ... and every combined row equals the oracle's weighted sum (identity experts: a token's K rows are its own)
+    for s in range(N):
+        tok = from_dev(tokens[s]).reshape(T, H)
+        w = G.uniform_f32(G.stream_key(SEED, s, 3), np.arange(T * K, dtype=np.uint64)).reshape(T, K)
+        want = OM.combine_rows(np.stack([tok] * K), w, "bf16")
+        assert_same(from_dev(out[s]).reshape(-1), want.reshape(-1), "bf16", f"source {s} combine, every row")
 
 
 def _fsdp2_layout(N):
