@@ -408,7 +408,9 @@ def _fsdp2_layout(N):
 def test_fsdp2_layer_full(N):
     """FSDP2 per-parameter reduce-scatter (avg, bf16 -> fp32) and all-gather of
     one transformer layer at full size, 64 ranks (every dim divides) and 48
-    ranks (uneven shards: 4096 / 48 and 11008 / 48 leave short last shards)."""
+    ranks (uneven shards: 4096 / 48 and 11008 / 48 leave short last shards):
+    sampled outputs against host-regenerated inputs, then every output of both
+    collectives."""
     rows, cols, offs, sh, soffs = _fsdp2_layout(N)
     P, S = len(rows), int(offs[-1])
     arena = gc.RankArena(N)
@@ -435,6 +437,16 @@ def test_fsdp2_layer_full(N):
             vals = np.stack([G.normal_bf16(gkeys[i], offs[p] + lo + k, 1e-3) for i in range(N)])
             want = SM.reduce_positions(vals, "bf16", np.full(len(k), (j + 1) % N), "avg", "fp32")
             assert_same(_gather(sviews[j][p], k), want, "fp32", f"param {p} owner {j}")
+    # every output of every parameter, owner by owner (shard j of parameter p is elements [lo, hi) of p on
+    # every rank, folded from rank j + 1; uneven at 48 ranks)
+    for p in range(P):
+        for j in range(N):
+            lo, hi = sh[j][p]
+            if hi == lo:
+                continue
+            a, b = int(offs[p]) + lo, int(offs[p]) + hi
+            want = SM.reduce_scatter_owner(_slices(grads, a, b), j, "bf16", "fp32", "avg", "ring")
+            assert_same(from_dev(sviews[j][p]), want, "fp32", f"param {p} owner {j}, every output")
     del grads, gsh, gviews, sviews
     psh = arena.alloc(most, "bf16")
     for r in range(N):
@@ -447,6 +459,9 @@ def test_fsdp2_layer_full(N):
     torch.cuda.synchronize()
     for d in range(1, N):
         assert torch.equal(params[d].view(torch.int16), params[0].view(torch.int16)), f"rank {d} differs"
+    for p in range(P):                                  # every output: parameter p is its shards in rank order
+        parts = [shviews[r][p] for r in range(N) if not isinstance(shviews[r][p], int)]
+        assert torch.equal(pviews[0][p].view(torch.int16), torch.cat(parts).view(torch.int16)), f"param {p}"
     for p in range(P):
         n = rows[p] * cols[p]
         e = np.unique(np.concatenate([rng.integers(0, n, size=4096), [0, n - 1]]))
