@@ -976,6 +976,12 @@ EXTRAS = (
     ("fsdp_layer_n64", "fsdp_layer_n64", "arena", 10, 3),
     ("moe_a2a_n8", "moe_a2a_n8", "arena", 20, 5),
     ("ddp_llama7b", "ddp_llama7b", "arena", 3, 1),
+    # the rows past the target's configurations, one workload each
+    ("ddp_llama7b_zero_copy", "ddp_llama7b_zero_copy", "arena", 3, 1),
+    ("moe_ep_n8", "moe_ep_n8", "arena", 20, 5),
+    ("fsdp2_layer_n64", "fsdp2_layer_n64", "arena", 10, 3),
+    ("hier_ar_n16", "hier_ar_n16", "arena", 20, 5),
+    ("hsdp_layer_n16", "hsdp_layer_n16", "arena", 10, 3),
 )
 
 
