@@ -970,18 +970,19 @@ def extra_line(w, steps, warmup):
 
 
 EXTRAS = (
-    # (key, workload, layout, steps, warmup)
-    ("ar_bf16_n8_separate", "ar_bf16_n8", "separate", 20, 5),
+    # (key, workload, layout, steps, warmup): at least 50 timed steps after 5 warm-up steps, except the
+    # 7B DDP passes (about 0.1 s each), which are timed over 3 full passes
+    ("ar_bf16_n8_separate", "ar_bf16_n8", "separate", 50, 10),
     ("ar_fp32_n4", "ar_fp32_n4", "arena", 50, 10),
-    ("fsdp_layer_n64", "fsdp_layer_n64", "arena", 10, 3),
-    ("moe_a2a_n8", "moe_a2a_n8", "arena", 20, 5),
+    ("fsdp_layer_n64", "fsdp_layer_n64", "arena", 50, 5),
+    ("moe_a2a_n8", "moe_a2a_n8", "arena", 50, 10),
     ("ddp_llama7b", "ddp_llama7b", "arena", 3, 1),
     # the rows past the target's configurations, one workload each
     ("ddp_llama7b_zero_copy", "ddp_llama7b_zero_copy", "arena", 3, 1),
-    ("moe_ep_n8", "moe_ep_n8", "arena", 20, 5),
-    ("fsdp2_layer_n64", "fsdp2_layer_n64", "arena", 10, 3),
-    ("hier_ar_n16", "hier_ar_n16", "arena", 20, 5),
-    ("hsdp_layer_n16", "hsdp_layer_n16", "arena", 10, 3),
+    ("moe_ep_n8", "moe_ep_n8", "arena", 50, 10),
+    ("fsdp2_layer_n64", "fsdp2_layer_n64", "arena", 50, 5),
+    ("hier_ar_n16", "hier_ar_n16", "arena", 50, 10),
+    ("hsdp_layer_n16", "hsdp_layer_n16", "arena", 50, 5),
 )
 
 
