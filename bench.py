@@ -489,8 +489,9 @@ class Fsdp2Workload(Workload):
         import numpy as np
         from gen import host as G
         from oracle import fsdp2 as F2
-        # q_proj and the two norm vectors, 64 ranks
-        rows, cols = [4096, 4096, 4096], [4096, 1, 1]
+        # q_proj's first 64 columns (the dim-0 shards of a column slice are those of the whole
+        # parameter) and the two norm vectors, 64 ranks
+        rows, cols = [4096, 4096, 4096], [64, 1, 1]
         n = [r * c for r, c in zip(rows, cols)]
         grads = [[G.normal_bf16(_keyed(seed, r, 0), np.arange(k, dtype=np.uint64) + 1000 * p, 1e-3)
                   for p, k in enumerate(n)] for r in range(self.N)]
@@ -498,7 +499,7 @@ class Fsdp2Workload(Workload):
         def run():
             return F2.reduce_scatter(grads, rows, cols, "bf16", "fp32", "avg", "ring")
         nbytes = self.N * sum(n) * 2 + sum(n) * 4
-        return run, nbytes, "oracle per-parameter ring reduce-scatter of 64 ranks x (q_proj 4096x4096 + 2 x 4096) bf16"
+        return run, nbytes, "oracle per-parameter ring reduce-scatter of 64 ranks x (q_proj[:, :64] + 2 x 4096) bf16"
 
 
 class HierWorkload(Workload):
@@ -539,7 +540,7 @@ class HierWorkload(Workload):
         import numpy as np
         from gen import host as G
         from oracle import hierarchical as H
-        m = 1 << 23  # the first quarter (8,388,608 elements) of each rank
+        m = 1 << 21  # the first 2,097,152 elements of each rank
         xs = [G.normal_bf16(_keyed(seed, r), np.arange(m, dtype=np.uint64), self.cfg["sigma"]) for r in range(self.N)]
 
         def run():
@@ -855,20 +856,20 @@ def host_cpu():
     return model, os.cpu_count()
 
 
-def cpu_baseline(w, seed):
+def cpu_baseline(w, seed, budget_s=10.0):
     run, nbytes, what = w.cpu_sample(seed)
     run()  # warm the code paths once (numpy allocations)
     t0 = time.perf_counter()
     reps = 0
-    while True:  # about 10 s of single-threaded oracle work
+    while True:  # about budget_s of single-threaded oracle work
         run()
         reps += 1
-        if time.perf_counter() - t0 >= 10.0 or reps >= 1000:
+        if time.perf_counter() - t0 >= budget_s or reps >= 1000:
             break
     per = (time.perf_counter() - t0) / reps
     model, threads = host_cpu()
     return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}; {reps} runs, {per:.3f} s each, single-threaded numpy",
+            "sample": f"{what}; {reps} runs, {per:.3g} s each, single-threaded numpy",
             "host_cpu": model, "host_threads": threads}
 
 
@@ -1016,6 +1017,9 @@ def run_extras(args):
                 "ms_per_step": round(ar, 4), "value": round(w.dominant_bytes / (ar * 1e-3) / 1e9, 2),
                 "unit": "GB/s (algorithmic: part of each freshly packed bucket is served by the 256 MB MALL)"}
             line["roofline"]["note"] = "the 226 bucket all-reduces launched alone (no pack before them): HBM-bound"
+        if not args.no_cpu and layout == "arena":
+            # the oracle beside each workload, on a bounded sample (about 3 s of work each)
+            line["cpu_baseline"] = cpu_baseline(w, args.seed, budget_s=3.0)
         out[key] = line
         del w
         pygc.collect()
