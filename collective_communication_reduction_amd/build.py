@@ -2,6 +2,7 @@
 
   collective_communication_reduction_amd/libgc.so   the collectives (C ABI in include/gc.h)
   gen/libgcgen.so                                   device twin of the input generator
+  tests/abi_c/abi_demo                              a plain C program using libgc through gc.h alone
 
 Usage: python collective_communication_reduction_amd/build.py  (or build() from Python).
 Every call recompiles; hipcc cross-compiles without a GPU.
@@ -78,7 +79,26 @@ def build(verbose=False):
     genlib = os.path.join(ROOT, "gen", "libgcgen.so")
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", genlib + ".tmp", gen_obj], verbose)
     os.replace(genlib + ".tmp", genlib)
-    return lib, genlib
+    demo = build_c_demo(verbose)
+    return lib, genlib, demo
+
+
+def build_c_demo(verbose=False):
+    """The C consumer of the ABI, compiled as C11 by the host C compiler (gc.h is a
+    C header) and linked against libgc.so and the HIP runtime."""
+    src = os.path.join(ROOT, "tests", "abi_c", "abi_demo.c")
+    out = os.path.join(ROOT, "tests", "abi_c", "abi_demo")
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for tests/abi_c/abi_demo.c")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    _run([cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+          f"-I{os.path.join(ROOT, 'include')}", "-isystem", os.path.join(rocm, 'include'), src, "-o", out + ".tmp",
+          f"-L{PKG}", "-lgc", f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/../../collective_communication_reduction_amd", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"],
+         verbose)
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
