@@ -83,6 +83,9 @@ def parse():
                    help="the default workload only: skip the other configurations' extra keys")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="also launch a plain device copy of this many MiB (counter calibration runs)")
+    p.add_argument("--patterns", action="store_true",
+                   help="instead of the bench line: each dominant kernel beside the unordered access pattern of "
+                        "its own reads and writes (bench_patterns.hip) on the same buffers")
     return p.parse_args()
 
 
@@ -1028,6 +1031,127 @@ def run_extras(args):
     return out
 
 
+def run_patterns(args):
+    """Each dominant kernel against the access-pattern kernels of bench_patterns.hip
+    on the same buffers, in one process, alternating over rounds: the pattern
+    moves the same bytes in the same tiles with no fold order and no floating
+    point, so the gap between the two is what the kernel itself costs.  Also
+    reads alone, writes alone and a 1 : 1 copy on two 2 GiB buffers."""
+    import ctypes
+    import gc as pygc
+    import statistics
+    import torch
+    import collective_communication_reduction_amd as gc
+    path = os.path.join(ROOT, "libbenchpatterns.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libbenchpatterns.so is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    VPP = ctypes.POINTER(ctypes.c_void_p)
+    lib.bp_pattern.restype = ctypes.c_int
+    lib.bp_pattern.argtypes = [VPP, ctypes.c_int, VPP, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rounds, steps, warm = 3, 20, 3
+
+    def pattern(sets, nvec, chunk_vecs=0, mode=0, out_mult=1):
+        """sets: list of (sources, destinations) tensor lists, rotated over the steps."""
+        ptrs = [(gc.gc_pointers(s) if s else None, gc.gc_pointers(d) if d else None, len(s), len(d))
+                for s, d in sets]
+
+        def run(k):
+            sp, dp, ns, nd = ptrs[k % len(ptrs)]
+            rc = lib.bp_pattern(sp, ns, dp, nd, nvec, chunk_vecs, mode, out_mult, sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"bp_pattern returned {rc}")
+        return run
+
+    def compare(label, entries):
+        """entries: (name, launch, bytes per launch); rounds alternate over the entries."""
+        rates = {name: [] for name, _, _ in entries}
+        for _ in range(rounds):
+            for name, fn, nbytes in entries:
+                ms = time_steps(fn, steps, warm)
+                rates[name].append(nbytes / (ms * 1e-3) / 1e9)
+        out = {"case": label, "rows": []}
+        for name, _, nbytes in entries:
+            r = rates[name]
+            med = statistics.median(r)
+            out["rows"].append({"kernel": name, "GBps": round(med, 1), "min": round(min(r), 1),
+                                "max": round(max(r), 1), "us": round(nbytes / med / 1e3, 1), "bytes": nbytes})
+        print(json.dumps(out), flush=True)
+        return out
+
+    def release():
+        pygc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    def ns(**kw):
+        a = argparse.Namespace(**vars(args))
+        a.algo, a.order, a.stagger, a.layout = "fused", "ring", None, "arena"
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    results = []
+    # plain streams on two 2 GiB buffers
+    n = 2 << 30
+    a_ = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b_ = torch.empty(n, dtype=torch.uint8, device="cuda")
+    nvec = n // 16
+
+    def lib_copy(_k):
+        gc.gc_all_to_all([a_], [b_], [[[1]]], n)
+    results.append(compare("2 GiB streams (one allocation each)", [
+        ("library segment copy (device-scope stores)", lib_copy, 2 * n),
+        ("pattern copy 1 in : 1 out", pattern([([a_], [b_])], nvec), 2 * n),
+        ("pattern reads alone", pattern([([a_], [])], nvec), n),
+        ("pattern writes alone", pattern([([], [b_])], nvec), n)]))
+    del a_, b_
+    release()
+
+    for layout in ("arena", "separate"):
+        w = make(ns(workload="ar_bf16_n8", layout=layout))
+        nv = w.S * 2 // 16
+        results.append(compare(f"ar_bf16_n8 ({w.layout})", [
+            ("library fused all-reduce", w.step, w.bytes_per_step),
+            ("pattern 8 in : 8 out", pattern(w.sets, nv), w.bytes_per_step),
+            ("pattern 8 in, no stores", pattern([(s, []) for s, _ in w.sets], nv), w.bytes_per_step // 2)]))
+        del w
+        release()
+
+    w = make(ns(workload="hier_ar_n16"))
+    nv = w.count * 2 // 16
+    results.append(compare(f"hier_ar_n16 ({w.layout})", [
+        ("library two-level all-reduce", w.step, w.bytes_per_step),
+        ("pattern 16 in : 16 out", pattern([(w.send, w.recv)], nv), w.bytes_per_step),
+        ("pattern 16 in, no stores", pattern([(w.send, [])], nv), w.bytes_per_step // 2)]))
+    del w
+    release()
+
+    w = make(ns(workload="fsdp_layer_n64"))
+    nv, cv = w.S * 2 // 16, w.rc * 2 // 16
+    rd = w.N * w.S * 2
+    results.append(compare(f"fsdp_layer_n64 reduce-scatter ({w.layout})", [
+        ("library reduce-scatter bf16 -> fp32", w.dominant_launch, w.rs_bytes),
+        ("pattern 64 in : owner's 2x out", pattern([(w.grads, w.gshards)], nv, cv, 1, 2), w.rs_bytes),
+        ("pattern 64 in, no stores", pattern([(w.grads, [])], nv), rd)]))
+    del w
+    release()
+
+    w = make(ns(workload="hsdp_layer_n16"))
+    nv, cv = w.S * 2 // 16, w.rc * 2 // 16
+    rd = w.N * w.S * 2
+    results.append(compare(f"hsdp_layer_n16 reduce-scatter ({w.layout})", [
+        ("library HSDP reduce-scatter bf16 -> fp32", lambda _k: w.rs(), w.rs_bytes),
+        ("pattern 16 in : both holders' 2x out", pattern([(w.grads, w.gshards)], nv, cv, 1, 2), w.rs_bytes),
+        ("pattern 16 in, no stores", pattern([(w.grads, [])], nv), rd)]))
+    del w
+    release()
+    print(json.dumps({"patterns": results, "rounds": rounds, "steps": steps, "warmup": warm}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -1036,6 +1160,9 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.init()
+    if args.patterns:
+        run_patterns(args)
+        return
     w = make(args)
     if args.calibrate_copy:
         n = args.calibrate_copy << 20

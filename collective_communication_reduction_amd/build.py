@@ -3,6 +3,7 @@
   collective_communication_reduction_amd/libgc.so   the collectives (C ABI in include/gc.h)
   gen/libgcgen.so                                   device twin of the input generator
   tests/abi_c/abi_demo                              a plain C program using libgc through gc.h alone
+  libbenchpatterns.so                               access-pattern ceilings for bench.py --patterns
 
 Usage: python collective_communication_reduction_amd/build.py  (or build() from Python).
 Every call recompiles; hipcc cross-compiles without a GPU.
@@ -70,17 +71,23 @@ def build(verbose=False):
     gen_src = os.path.join(ROOT, "gen", "device.hip")
     gen_obj = os.path.join(BUILD, "gen_device.o")
     jobs.append((gen_src, gen_obj))
+    pat_src = os.path.join(ROOT, "bench_patterns.hip")
+    pat_obj = os.path.join(BUILD, "bench_patterns.o")
+    jobs.append((pat_src, pat_obj))
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda j: _compile(hipcc, j[0], j[1], includes, verbose), jobs))
     lib = os.path.join(PKG, "libgc.so")
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", lib + ".tmp"]
-         + [o for s, o in jobs if s != gen_src], verbose)
+         + [o for s, o in jobs if s not in (gen_src, pat_src)], verbose)
     os.replace(lib + ".tmp", lib)
     genlib = os.path.join(ROOT, "gen", "libgcgen.so")
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", genlib + ".tmp", gen_obj], verbose)
     os.replace(genlib + ".tmp", genlib)
+    patlib = os.path.join(ROOT, "libbenchpatterns.so")
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", patlib + ".tmp", pat_obj], verbose)
+    os.replace(patlib + ".tmp", patlib)
     demo = build_c_demo(verbose)
-    return lib, genlib, demo
+    return lib, genlib, patlib, demo
 
 
 def build_c_demo(verbose=False):

@@ -1,8 +1,11 @@
-"""bench.py's command-line contract that holds without a GPU: it measures one GPU and says so."""
+"""bench.py's command-line contract that holds without a GPU (it measures one GPU and says so),
+and the host checks of its pattern kernels."""
 
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -22,3 +25,34 @@ def test_every_workload_has_a_kernel_source_list():
         for rel in bench.KERNEL_SOURCES[bench.WORKLOAD_KERNELS[w]]:
             assert os.path.exists(os.path.join(ROOT, rel)), rel
         assert len(bench.kernel_hash(w)) == 16
+
+
+def test_pattern_kernel_refuses_bad_arguments():
+    """bench_patterns.hip's host checks (no GPU needed: every call below is refused
+    before anything is launched)."""
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "libbenchpatterns.so")
+    if not os.path.exists(path):
+        pytest.skip("libbenchpatterns.so is not built")
+    lib = ctypes.CDLL(path)
+    VPP = ctypes.POINTER(ctypes.c_void_p)
+    lib.bp_pattern.restype = ctypes.c_int
+    lib.bp_pattern.argtypes = [VPP, ctypes.c_int, VPP, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    arr = (ctypes.c_void_p * 64)(*([0x10000] * 64))
+    sink = ctypes.c_void_p(0x20000)
+    cases = [
+        (arr, 65, arr, 1, 64, 0, 0, 1),          # too many sources
+        (arr, 0, arr, 0, 64, 0, 0, 1),           # nothing to do
+        (arr, 1, arr, 1, 0, 0, 0, 1),            # no vectors
+        (arr, 1, arr, 1, 64, 0, 2, 1),           # unknown mode
+        (arr, 8, arr, 8, 100, 30, 1, 2),         # chunks do not divide the length
+        (arr, 8, arr, 6, 64, 8, 1, 2),           # 8 chunks, 6 destinations
+        (arr, 8, arr, 8, 64, 8, 1, 5),           # output multiple out of range
+    ]
+    for src, ns, dst, nd, nvec, cv, mode, om in cases:
+        assert lib.bp_pattern(src, ns, dst, nd, nvec, cv, mode, om, sink, None) == 1
+    mis = (ctypes.c_void_p * 2)(0x10000, 0x10008)  # second source not 16-byte aligned
+    assert lib.bp_pattern(mis, 2, arr, 1, 64, 0, 0, 1, sink, None) == 1
+    assert lib.bp_pattern(arr, 1, arr, 1, 64, 0, 0, 1, None, None) == 1   # no sink
