@@ -29,10 +29,18 @@ struct Span {
 
 Span span(const void* p, uint64_t bytes) { return Span{addr(p), addr(p) + bytes}; }
 
-// True if `bytes` bytes at p end inside the 64-bit address space.  Every
-// buffer extent a call derives is checked with it before any span is formed,
-// so spans never wrap and the addresses handed to the kernels never overflow.
-bool fits(const void* p, uint64_t bytes) { return bytes <= UINT64_MAX - addr(p); }
+// Largest extent of one buffer: 2^40 bytes, beyond any one GPU's memory
+// (MI355X: 288 GB of HBM).  With it, and a call's total copy volume bounded by
+// kMaxCopyBytes, every tile count the planners derive (2 KiB or more per
+// tile) stays below 2^32.
+constexpr uint64_t kMaxExtent = uint64_t(1) << 40;
+constexpr uint64_t kMaxCopyBytes = uint64_t(1) << 42;
+
+// True if `bytes` bytes at p are a possible buffer: at most kMaxExtent and
+// ending inside the 64-bit address space.  Every buffer extent a call derives
+// is checked with it before any span is formed, so spans never wrap and the
+// addresses handed to the kernels never overflow.
+bool fits(const void* p, uint64_t bytes) { return bytes <= kMaxExtent && bytes <= UINT64_MAX - addr(p); }
 
 // Address `off` bytes past p, computed on integers (the extent holding it was checked with fits).
 void* at(const void* p, uint64_t off) { return reinterpret_cast<void*>(addr(p) + off); }
@@ -335,6 +343,8 @@ extern "C" gc_status gc_all_to_all(const void* const* send, void* const* recv, c
   for (int r = 0; r < N; ++r)
     for (int s = 0; s < N; ++s)
       if (overlaps(all[r], span(send[s], send_rows[s] * row_bytes))) return GC_ERR_INVALID_ARG;
+  if (mul_overflows(static_cast<uint64_t>(total), row_bytes) || static_cast<uint64_t>(total) * row_bytes > kMaxCopyBytes)
+    return GC_ERR_UNSUPPORTED;
 
   // Every (s, d, e) block is contiguous in send[s] and in recv[d]: the
   // all-to-all is one contiguous copy per non-empty block, done by the
@@ -786,6 +796,7 @@ extern "C" gc_status gc_bucket_plan_create(const size_t* numels, int ntensors, g
     p->tensor_offset.assign(ntensors, 0);
     std::vector<int> cur;
     size_t cur_elems = 0;
+    bool too_big = false;  // a bucket larger than any one GPU's buffer
     auto close = [&]() {
       size_t run = 0;
       for (int ti : cur) {
@@ -796,6 +807,7 @@ extern "C" gc_status gc_bucket_plan_create(const size_t* numels, int ntensors, g
       p->buckets.push_back(cur);
       p->used.push_back(run);
       p->padded.push_back((run + pad_to - 1) / pad_to * pad_to);
+      if (p->padded.back() * p->es > kMaxExtent) too_big = true;
       cur.clear();
       cur_elems = 0;
     };
@@ -813,6 +825,10 @@ extern "C" gc_status gc_bucket_plan_create(const size_t* numels, int ntensors, g
       if (cap_bytes != SIZE_MAX && cur_elems * p->es >= cap_bytes) close();
     }
     if (!cur.empty()) close();
+    if (too_big) {
+      delete p;
+      return GC_ERR_INVALID_ARG;
+    }
   } catch (const std::bad_alloc&) {
     delete p;
     return GC_ERR_NO_MEMORY;

@@ -26,6 +26,10 @@
  *   - No call memsets, copies through the host or synchronises, so calls can
  *     be captured into a HIP graph and replayed (validation runs at capture).
  *   - nranks is 1..GC_MAX_RANKS.  Element counts are per rank.
+ *   - Every buffer extent a call derives from its counts is at most 2^40
+ *     bytes (more than one GPU holds) and ends inside the address space;
+ *     otherwise GC_ERR_INVALID_ARG.  An all-to-all moves at most 2^42 bytes
+ *     per call (GC_ERR_UNSUPPORTED above).
  *   - Calls are reentrant; concurrent calls on different streams must not
  *     write overlapping memory.
  *

@@ -164,6 +164,27 @@ def test_bucket_pack_validation():
         gc.gc_bucket_plan_create([1 << 62], "bf16", gc.SIZE_MAX)
 
 
+def test_extent_and_copy_volume_limits():
+    """No buffer extent beyond 2^40 bytes (more than any one GPU holds) and no all-to-all moving more than
+    2^42 bytes in one call: both are refused on the host, which keeps every planned tile count in 32 bits."""
+    big = (1 << 39) + 8                                   # bf16 elements: 2^40 + 16 bytes
+    s, r = _ptrs(2, step=1 << 41), _ptrs(2, step=1 << 41, base=FAKE + (1 << 44))
+    assert _status(gc.gc_all_reduce, s, r, count=big, dtype="bf16", stream=0) == gc.GC_ERR_INVALID_ARG
+    assert _status(gc.gc_reduce_scatter, s, r, recv_count=big // 2, in_dtype="bf16", out_dtype="bf16",
+                   stream=0) == gc.GC_ERR_INVALID_ARG
+    assert _status(gc.gc_all_gather, s, r, count=big // 2, dtype="bf16", stream=0) == gc.GC_ERR_INVALID_ARG
+    assert _status(gc.gc_hier_all_reduce, _ptrs(4, step=1 << 41), _ptrs(4, step=1 << 41, base=FAKE + (1 << 44)),
+                   2, count=big, dtype="bf16", stream=0) == gc.GC_ERR_INVALID_ARG
+    # 8 ranks each sending 2^40 bytes (2^25 rows of 4 KiB to every rank): every buffer is possible, the
+    # call's 2^43 bytes are not
+    N, rows = 8, 1 << 25
+    splits = [[[rows] for _ in range(N)] for _ in range(N)]
+    send, recv = _ptrs(N, step=1 << 41), _ptrs(N, step=1 << 41, base=FAKE + (1 << 45))
+    assert _status(gc.gc_all_to_all, send, recv, splits, 4096, stream=0) == gc.GC_ERR_UNSUPPORTED
+    with pytest.raises(gc.GcError):
+        gc.gc_bucket_plan_create([8, big], "bf16", gc.SIZE_MAX)   # one bucket of 2^40 + 32 bytes
+
+
 def test_rank_buffers_layout():
     # host tensors stand in for device memory: only the offsets are checked
     bufs = gc.gc_rank_buffers(8, 1000, "bf16", device="cpu", stagger_bytes=4096, slot_align=1 << 20)

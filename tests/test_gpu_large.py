@@ -1,5 +1,5 @@
-"""GPU parity past 2^31 elements per rank: the sizes where a 32-bit element or
-byte index would wrap.  Each call is checked on sampled outputs (random
+"""GPU parity past 2^31 (and 2^32) elements per rank: the sizes where a 32-bit
+element or byte index would wrap.  Each call is checked on sampled outputs (random
 positions, every chunk edge, and the positions around 2^31 and 2^32 bytes)
 that the oracle computes one by one from inputs it regenerates on the host."""
 
@@ -95,6 +95,34 @@ def test_reduce_scatter_and_all_gather_past_2_31_elements():
     want = np.array([vals[o, k] for k, o in enumerate(owner)], dtype=np.uint16)
     for d in range(N):
         assert_same(_gather(full[d], pos), want, "bf16", f"all-gather rank {d}")
+
+
+def test_all_reduce_and_reduce_scatter_past_2_32_elements():
+    """Past 2^32 elements per rank (8 GiB of bf16): a 32-bit element count or vector index would wrap here.
+    The fused all-reduce and the bf16 -> fp32 reduce-scatter (whose owner chunks exceed 2^31 elements)."""
+    N, S = 2, (1 << 32) + 10
+    edges = [(1 << 32) - 1, 1 << 32, (1 << 32) + 1, (1 << 32) + 9]
+    keys, send = _filled(N, S, "bf16", seed=43)
+    recv = [torch.empty_like(send[0]) for _ in range(N)]
+    print(f"all-reduce bf16 avg, {N} ranks x {S} elements", flush=True)
+    gc.gc_all_reduce(send, recv, op="avg", order="ring")
+    torch.cuda.synchronize()
+    pos = _positions(S, N, np.random.default_rng(3), edges)
+    vals = _host_values(keys, pos, "bf16")
+    want = SM.all_reduce_at(vals, pos, S, "bf16", "avg", "ring")
+    for r in range(N):
+        assert_same(_gather(recv[r], pos), want, "bf16", f"rank {r}")
+    del recv
+    torch.cuda.empty_cache()
+    rc = S // N                                     # 2^31 + 5 elements per owner
+    shards = [torch.empty(rc, dtype=torch.float32, device=DEV) for _ in range(N)]
+    print(f"reduce-scatter bf16 -> fp32 avg, {N} ranks x {rc} per owner", flush=True)
+    gc.gc_reduce_scatter(send, shards, op="avg", order="ring")
+    torch.cuda.synchronize()
+    want = SM.reduce_scatter_at(vals, pos // rc, pos % rc, rc, "bf16", "fp32", "avg", "ring")
+    for j in range(N):
+        sel = pos // rc == j
+        assert_same(_gather(shards[j], pos[sel] % rc), want[sel], "fp32", f"owner {j}")
 
 
 def test_two_level_all_reduce_past_2_31_elements():
