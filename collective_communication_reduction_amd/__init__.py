@@ -410,10 +410,15 @@ def gc_moe_route_noalloc(experts, ntokens, topk, experts_per_rank, splits, dest,
     Calls that overlap on one GPU share that scratch and race."""
     n = len(ntokens)
     nsplit = n * n * max(0, int(experts_per_rank)) * 8
-    _check(_c_moe_route_noalloc(_bufs(experts, n, _per_route(ntokens, topk, 4), "experts"), _i64_array(ntokens), n,
-                                int(topk), int(experts_per_rank), _buf(splits, nsplit, "splits"),
-                                _bufs(dest, n, _per_route(ntokens, topk, 8), "dest"), _stream(stream, splits)),
-           "gc_moe_route_noalloc")
+    st = _c_moe_route_noalloc(_bufs(experts, n, _per_route(ntokens, topk, 4), "experts"), _i64_array(ntokens), n,
+                              int(topk), int(experts_per_rank), _buf(splits, nsplit, "splits"),
+                              _bufs(dest, n, _per_route(ntokens, topk, 8), "dest"), _stream(stream, splits))
+    if st == GC_ERR_UNSUPPORTED:
+        need = gc_moe_route_scratch_bytes(ntokens, topk, experts_per_rank)
+        if need > GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES:
+            raise GcError(st, f"gc_moe_route_noalloc (the plan needs {need} bytes of scratch, the static scratch "
+                              f"holds {GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES}; use gc_moe_route with a scratch buffer)")
+    _check(st, "gc_moe_route_noalloc")
     return splits, dest
 
 

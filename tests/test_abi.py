@@ -260,6 +260,8 @@ def test_moe_route_noalloc_validation():
     assert gc.gc_moe_route_scratch_bytes(big, 8, 64) > gc.GC_MOE_ROUTE_NOALLOC_SCRATCH_BYTES
     assert st(experts=_ptrs(8), ntokens=big, topk=8, experts_per_rank=64,
               dest=_ptrs(8, base=FAKE + (1 << 40))) == gc.GC_ERR_UNSUPPORTED
+    with pytest.raises(gc.GcError, match="needs .* bytes of scratch"):          # the refusal says why
+        route(_ptrs(8), big, 8, 64, sp, _ptrs(8, base=FAKE + (1 << 40)), stream=0)
     assert st(splits=sp + 4) == gc.GC_ERR_INVALID_ARG
     assert st(dest=de[:2] + [de[2] + 4]) == gc.GC_ERR_INVALID_ARG
     assert st(experts=[ex[0], ex[1], 0]) == gc.GC_ERR_INVALID_ARG
