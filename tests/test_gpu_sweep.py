@@ -1,4 +1,5 @@
-"""Seeded random sweep of the reduction calls against the oracle: rank counts
+"""Seeded random sweep of the reduction calls (flat, two-level, HSDP, FSDP2 and
+the zero-copy bucket all-reduce) against the oracle: rank counts
 (odd, prime, up to 64), lengths from empty to a few hundred thousand elements
 (log-uniform, so ragged tails and short chunks are common), element types,
 ops, fold orders, both all-reduce algorithms, buffer views starting a few
@@ -297,3 +298,73 @@ def test_fsdp2_sweep(seed):
     for d in _sample_ranks(N):
         for p in range(P):
             assert_same(from_dev(full[d][p]), want_full[d][p], tout, f"{case} all-gather rank {d} param {p}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_bucket_all_reduce_sweep(seed):
+    """The zero-copy bucket all-reduce on random tensor lists (empty and one-element
+    tensors included), caps, paddings (1 or N: the FlatParameter case), types, ops
+    and fold orders, with the tensors as views at random element offsets inside
+    one sentinel-guarded allocation per rank (sometimes shifted by one element on
+    odd ranks, so pieces take the element path): every tensor on every sampled
+    rank against the oracle's pack -> all-reduce -> unpack, the elements between
+    the tensors untouched, and the sum of squares against its exact value."""
+    from oracle import buckets as OB
+    rng = np.random.default_rng(13000 + seed)
+    N = int(rng.choice(RANKS))
+    T = int(rng.integers(1, 30 if N <= 8 else 8))
+    numels = [_length(rng, 40_000) for _ in range(T)]
+    if rng.random() < 0.3:
+        numels[int(rng.integers(T))] = 0
+    dtype, _, op = REDUCE_TYPES[int(rng.integers(len(REDUCE_TYPES)))]
+    order = str(rng.choice(["ring", "rank", "ring_wire"]))
+    pad = int(rng.choice([1, N]))
+    es = 4 if dtype != "bf16" else 2
+    cap = int(rng.integers(1, max(2, sum(numels) + 1))) * es
+    shift = [r % 2 for r in range(N)] if rng.random() < 0.25 else [0] * N
+    offs, run = [], int(rng.integers(0, 8))
+    for n in numels:
+        offs.append(run)
+        run += n + int(rng.integers(0, 5))
+    case = f"N={N} numels={numels} {dtype} {op} {order} pad={pad} cap={cap} shift={shift[:2]}"
+    host = [[_values(dtype, 1, n, seed * 1000 + r * 53 + t)[0] for t, n in enumerate(numels)] for r in range(N)]
+    flat = _views(run + 1, dtype, [0] * N)
+    dev = [[flat[r][shift[r] + offs[t]:shift[r] + offs[t] + numels[t]] for t in range(T)] for r in range(N)]
+    for r in range(N):
+        for t in range(T):
+            if numels[t]:
+                dev[r][t].copy_(to_dev(host[r][t], dtype))
+    torch.cuda.synchronize()
+    before = {r: _ints(flat[r]._base).cpu().numpy().copy() for r in _sample_ranks(N)}
+    plan = gc.BucketPlan(numels, dtype, cap, reverse=True, pad_to=pad)
+    try:
+        buckets = OB.assign_buckets(numels, es, cap, reverse=True)
+        assert plan.nbuckets == len(buckets), case
+        sq = torch.zeros(1, dtype=torch.float64, device=DEV)
+        use_sq = dtype != "int32"
+        ptrs = [dev[r][t] if numels[t] else None for r in range(N) for t in range(T)]
+        for b in range(plan.nbuckets):
+            plan.all_reduce(b, ptrs, N, op=op, order=order, sumsq=sq if use_sq else None)
+        torch.cuda.synchronize()
+        exact = 0
+        for b, ts in enumerate(buckets):
+            want = OB.bucket_all_reduce(host, ts, numels, dtype, op, order, pad_to=pad)
+            for t in ts:
+                if not numels[t]:
+                    continue
+                for r in _sample_ranks(N):
+                    _check(from_dev(dev[r][t]), want[r][t], dtype, f"{case} bucket {b} tensor {t} rank {r}")
+                if use_sq:
+                    exact += OB.sum_of_squares(want[0][t], dtype)
+        # the elements between the tensors, before the first and after the last keep what they held
+        for r in _sample_ranks(N):
+            now = _ints(flat[r]._base).cpu().numpy()
+            inside = np.zeros(now.size, dtype=bool)
+            for o, n in zip(offs, numels):
+                inside[shift[r] + o:shift[r] + o + n] = True
+            assert np.array_equal(now[~inside], before[r][~inside]), f"{case}: rank {r} wrote outside its tensors"
+        if use_sq:
+            got = float(sq.item())
+            assert abs(got - float(exact)) <= 1e-12 * float(exact) + 1e-300, case
+    finally:
+        plan.close()

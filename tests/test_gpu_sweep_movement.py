@@ -3,7 +3,8 @@ guard bytes around every destination: the all-to-all(v) and the DDP bucket
 pack / unpack, over random rank and expert counts, row sizes from one byte to
 a few KiB, tensor lists with empty and one-element tensors, caps, padding, and
 buffers starting at random byte or element offsets (so both the 16-byte and the
-narrow copy paths run, with every head / tail length).  Movement is checked
+narrow copy paths run, with every head / tail length); and the MoE routing plan,
+dispatch and combine over random routings.  Movement is checked
 bit for bit, and every byte outside the destinations must keep its sentinel
 (a store past a destination's end, or before its start, fails here).  Each case
 is drawn from its own seed, printed in the test id."""
@@ -151,3 +152,56 @@ def test_bucket_pack_unpack_sweep(seed):
             assert np.array_equal(_bits(src[r], dtype)[offs_in[0]:offs_in[0] + numels[0]], host[r][0]), case
     finally:
         plan.close()
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_moe_route_dispatch_combine_sweep(seed):
+    """The expert-parallel chain on random shapes: rank and expert counts, ragged
+    and empty sources, one to eight experts per token, dropped routes, row widths
+    that take the 16-byte and the narrow paths, bf16 or fp32 rows.  The device plan
+    must equal the oracle's route for route, every dispatched row must be the
+    token row its route names (bit for bit, nothing written past the planned
+    rows), and the weighted combine of those rows (identity experts) must equal
+    the oracle's combine of its own dispatch."""
+    from oracle import moe as M
+    from tests.gpu_util import assert_same, from_dev, to_dev
+    from tests.test_gpu_moe import _expert_rows, _routing, check_plan, route_on_device
+    rng = np.random.default_rng(14000 + seed)
+    N = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    E = int(rng.choice([1, 2, 3, 4, 8]))
+    K = int(rng.integers(1, min(8, N * E) + 1))
+    T = [_length(rng, 3000) for _ in range(N)]
+    drop = float(rng.choice([0.0, 0.0, 0.05]))
+    dtype = str(rng.choice(["bf16", "fp32"]))
+    H = _length(rng, 700) + 1 if rng.random() < 0.7 else int(rng.choice([1024, 4096, 4100]))
+    while sum(T) * K * H > 4_000_000:                 # keep the oracle's side to a few seconds
+        T = [t // 2 for t in T]
+    es = 2 if dtype == "bf16" else 4
+    case = f"N={N} E={E} K={K} T={T[:4]} drop={drop} {dtype} H={H}"
+    experts = _routing(rng, N, E, T, K, drop)
+    ntok, splits, dest = route_on_device(experts, N, E, K)
+    want_splits = check_plan(experts, N, E, K, splits, dest)
+    rows = [int(r) for r in want_splits.sum(axis=(0, 2))]
+    tokens = [_expert_rows(rng, t, H, dtype, special=False) for t in T]
+    tok_dev = [to_dev(t, dtype) if t.size else torch.empty(1, dtype=TORCH[dtype], device=DEV) for t in tokens]
+    spare = 2
+    recv = [torch.full(((r + spare) * H,), 3.0, dtype=TORCH[dtype], device=DEV) for r in rows]
+    gc.gc_moe_dispatch(tok_dev, ntok, dest, K, H * es, recv, [r + spare for r in rows])
+    torch.cuda.synchronize()
+    want_recv = M.dispatch(tokens, experts, N, E, H)
+    for d in range(N):
+        got = from_dev(recv[d])
+        assert_same(got[:rows[d] * H], want_recv[d], dtype, f"{case} dispatch to rank {d}")
+        assert np.all(got[rows[d] * H:] == from_dev(torch.full((spare * H,), 3.0, dtype=TORCH[dtype], device=DEV))), \
+            f"{case}: dispatch wrote past rank {d}'s rows"
+    w = [rng.normal(size=(t, K)).astype(np.float32) for t in T]
+    want = M.combine(want_recv, experts, w, N, E, H, dtype)
+    out = [torch.full((t * H + 16,), 5.0, dtype=TORCH[dtype], device=DEV) for t in T]
+    gc.gc_moe_combine(recv, [r + spare for r in rows], dest, [torch.from_numpy(x.reshape(-1)).to(DEV) for x in w],
+                      ntok, K, H, dtype, [o[:t * H] for o, t in zip(out, T)])
+    torch.cuda.synchronize()
+    for s in range(N):
+        got = from_dev(out[s])
+        assert_same(got[:T[s] * H], want[s], dtype, f"{case} combine for source {s}")
+        assert np.all(got[T[s] * H:] == from_dev(torch.full((16,), 5.0, dtype=TORCH[dtype], device=DEV))), \
+            f"{case}: combine wrote past source {s}'s rows"
