@@ -99,6 +99,29 @@ def test_all_reduce_in_place(dtype, N):
             _check(from_dev(bufs[r]), want, dtype, f"in place {algo}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind", ["fused", "rs_ag", "two_level"])
+def test_all_reduce_into_another_ranks_input(dtype, kind):
+    """recv[r] may be exactly another rank's send buffer (here send[(r + 3) mod N]): every
+    element's inputs are read before any of its outputs is written, so the result is
+    the same as out of place."""
+    N, S = 8, 4096 * 5 + 3
+    xs = _gen(dtype, N, S, seed=13)
+    bufs = [to_dev(x, dtype) for x in xs]
+    recv = [bufs[(r + 3) % N] for r in range(N)]
+    if kind == "two_level":
+        from oracle import hierarchical as H
+        want = H.all_reduce(xs, 4, dtype, "avg", "ring")[0]
+        gc.gc_hier_all_reduce(bufs, recv, 4, op="avg", order="ring")
+    else:
+        want = C.all_reduce(xs, dtype, "avg", "ring")[0]
+        scratch = torch.empty(gc.gc_all_reduce_scratch_bytes(S, N, dtype), dtype=torch.uint8, device=DEV)
+        gc.gc_all_reduce(bufs, recv, op="avg", algo=kind, scratch=scratch)
+    torch.cuda.synchronize()
+    for r in range(N):
+        _check(from_dev(bufs[r]), want, dtype, f"{kind} buffer {r}")
+
+
 @pytest.mark.parametrize("offsets", [(1, 1, 1, 1), (3, 3, 3, 3), (0, 1, 2, 3), (5, 0, 5, 0)])
 @pytest.mark.parametrize("order", ["ring", "ring_wire"])
 def test_all_reduce_misaligned_views(offsets, order):
