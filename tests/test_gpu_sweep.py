@@ -14,6 +14,8 @@ allocation filled with a sentinel: after the call nothing outside the views
 may have changed, and inputs (outside an in-place output) must still hold
 their values."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -25,6 +27,11 @@ from oracle import hierarchical as H
 from tests.gpu_util import DEV, assert_same, empty, from_dev, max_ulp, to_dev
 
 pytestmark = pytest.mark.gpu
+
+
+def _seeds(n):
+    """The sweep's seeds: n by default; GC_SWEEP_SCALE=k runs k * n cases (the first n are the default ones)."""
+    return range(n * max(1, int(os.environ.get("GC_SWEEP_SCALE", "1"))))
 
 RANKS = [1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 31, 33, 63, 64]
 REDUCE_TYPES = [("bf16", "bf16", "avg"), ("bf16", "bf16", "sum"), ("fp32", "fp32", "sum"), ("fp32", "fp32", "avg"),
@@ -101,7 +108,7 @@ def _sample_ranks(N):
     return sorted({0, N // 2, N - 1})
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", _seeds(48))
 def test_all_reduce_sweep(seed):
     rng = np.random.default_rng(7000 + seed)
     N = int(rng.choice(RANKS))
@@ -130,7 +137,7 @@ def test_all_reduce_sweep(seed):
         _unchanged([send[r] for r in _sample_ranks(N)], [xs[r] for r in _sample_ranks(N)], dtype, case)
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", _seeds(48))
 def test_reduce_scatter_sweep(seed):
     rng = np.random.default_rng(8000 + seed)
     N = int(rng.choice(RANKS))
@@ -166,7 +173,7 @@ def test_reduce_scatter_sweep(seed):
         _untouched(recv, case)
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", _seeds(32))
 def test_all_gather_sweep(seed):
     rng = np.random.default_rng(9000 + seed)
     N = int(rng.choice(RANKS))
@@ -194,7 +201,7 @@ def test_all_gather_sweep(seed):
         _unchanged([send[r] for r in _sample_ranks(N)], [shards[r] for r in _sample_ranks(N)], dtype, case)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_two_level_all_reduce_sweep(seed):
     rng = np.random.default_rng(10000 + seed)
     N = int(rng.choice([2, 4, 6, 8, 9, 12, 16, 32, 64]))
@@ -220,7 +227,7 @@ def test_two_level_all_reduce_sweep(seed):
     _unchanged([send[r] for r in _sample_ranks(N)], [xs[r] for r in _sample_ranks(N)], dtype, case)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_hsdp_reduce_scatter_sweep(seed):
     rng = np.random.default_rng(11000 + seed)
     N = int(rng.choice([2, 4, 6, 8, 9, 12, 16, 32, 64]))
@@ -258,7 +265,7 @@ def test_hsdp_reduce_scatter_sweep(seed):
         _untouched(recv, case)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_fsdp2_sweep(seed):
     """Random parameter lists (including rows < N, so trailing ranks hold empty
     shards, and empty parameters): per-parameter dim-0 reduce-scatter, then the
@@ -300,7 +307,7 @@ def test_fsdp2_sweep(seed):
             assert_same(from_dev(full[d][p]), want_full[d][p], tout, f"{case} all-gather rank {d} param {p}")
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_bucket_all_reduce_sweep(seed):
     """The zero-copy bucket all-reduce on random tensor lists (empty and one-element
     tensors included), caps, paddings (1 or N: the FlatParameter case), types, ops

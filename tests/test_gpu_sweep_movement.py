@@ -9,6 +9,8 @@ bit for bit, and every byte outside the destinations must keep its sentinel
 (a store past a destination's end, or before its start, fails here).  Each case
 is drawn from its own seed, printed in the test id."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,6 +21,11 @@ from oracle import collectives as C
 from tests.gpu_util import DEV, TORCH
 
 pytestmark = pytest.mark.gpu
+
+
+def _seeds(n):
+    """The sweep's seeds: n by default; GC_SWEEP_SCALE=k runs k * n cases (the first n are the default ones)."""
+    return range(n * max(1, int(os.environ.get("GC_SWEEP_SCALE", "1"))))
 
 GUARD = 64                 # sentinel bytes after every destination
 ES = {"bf16": 2, "fp32": 4, "int32": 4}
@@ -34,7 +41,7 @@ def _bytes_view(nbytes, off, fill):
     return full, full[off:off + nbytes]
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_all_to_all_sweep(seed):
     rng = np.random.default_rng(13000 + seed)
     N = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 64]))
@@ -85,7 +92,7 @@ def _bits(t, dtype):
     return t.view(torch.int32).cpu().numpy().view(np.uint32)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_bucket_pack_unpack_sweep(seed):
     rng = np.random.default_rng(14000 + seed)
     N = int(rng.choice([1, 2, 3, 4, 8]))
@@ -154,7 +161,7 @@ def test_bucket_pack_unpack_sweep(seed):
         plan.close()
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", _seeds(24))
 def test_moe_route_dispatch_combine_sweep(seed):
     """The expert-parallel chain on random shapes: rank and expert counts, ragged
     and empty sources, one to eight experts per token, dropped routes, row widths
