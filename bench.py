@@ -996,6 +996,7 @@ def run_extras(args):
     import gc as pygc
     import torch
     out = {}
+    pats = Patterns()
     for key, name, layout, steps, warmup in EXTRAS:
         a = argparse.Namespace(**vars(args))
         a.workload, a.layout, a.algo, a.order, a.stagger = name, layout, "fused", "ring", None
@@ -1020,6 +1021,9 @@ def run_extras(args):
                 "ms_per_step": round(ar, 4), "value": round(w.dominant_bytes / (ar * 1e-3) / 1e9, 2),
                 "unit": "GB/s (algorithmic: part of each freshly packed bucket is served by the 256 MB MALL)"}
             line["roofline"]["note"] = "the 226 bucket all-reduces launched alone (no pack before them): HBM-bound"
+        side = pats.beside(w)
+        if side is not None:
+            line["pattern"] = side
         if not args.no_cpu and layout == "arena":
             # the oracle beside each workload, on a bounded sample (about 3 s of work each)
             line["cpu_baseline"] = cpu_baseline(w, args.seed, budget_s=3.0)
@@ -1031,43 +1035,73 @@ def run_extras(args):
     return out
 
 
-def run_patterns(args):
-    """Each dominant kernel against the access-pattern kernels of bench_patterns.hip
-    on the same buffers, in one process, alternating over rounds: the pattern
-    moves the same bytes in the same tiles with no fold order and no floating
-    point, so the gap between the two is what the kernel itself costs.  Also
-    reads alone, writes alone and a 1 : 1 copy on two 2 GiB buffers."""
-    import ctypes
-    import gc as pygc
-    import statistics
-    import torch
-    import collective_communication_reduction_amd as gc
-    path = os.path.join(ROOT, "libbenchpatterns.so")
-    if not os.path.exists(path):
-        raise RuntimeError("libbenchpatterns.so is missing: run __graft_entry__.build() first")
-    lib = ctypes.CDLL(path)
-    VPP = ctypes.POINTER(ctypes.c_void_p)
-    lib.bp_pattern.restype = ctypes.c_int
-    lib.bp_pattern.argtypes = [VPP, ctypes.c_int, VPP, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
-                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream().cuda_stream
-    rounds, steps, warm = 3, 20, 3
+class Patterns:
+    """The access-pattern kernels of bench_patterns.hip (libbenchpatterns.so): unordered
+    kernels that move the same bytes as a collective, in the same tiles, with no fold
+    order and no floating point, so that a kernel can be timed beside the pattern of its
+    own reads and writes on the same buffers."""
 
-    def pattern(sets, nvec, chunk_vecs=0, mode=0, out_mult=1):
-        """sets: list of (sources, destinations) tensor lists, rotated over the steps."""
+    def __init__(self):
+        import ctypes
+        import torch
+        import collective_communication_reduction_amd as gc
+        path = os.path.join(ROOT, "libbenchpatterns.so")
+        if not os.path.exists(path):
+            raise RuntimeError("libbenchpatterns.so is missing: run __graft_entry__.build() first")
+        self.gc = gc
+        self.lib = ctypes.CDLL(path)
+        VPP = ctypes.POINTER(ctypes.c_void_p)
+        self.lib.bp_pattern.restype = ctypes.c_int
+        self.lib.bp_pattern.argtypes = [VPP, ctypes.c_int, VPP, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        self.sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def pattern(self, sets, nvec, chunk_vecs=0, mode=0, out_mult=1):
+        """A launch of the pattern over sets, a list of (sources, destinations) tensor lists rotated over the steps."""
+        gc = self.gc
         ptrs = [(gc.gc_pointers(s) if s else None, gc.gc_pointers(d) if d else None, len(s), len(d))
                 for s, d in sets]
 
         def run(k):
             sp, dp, ns, nd = ptrs[k % len(ptrs)]
-            rc = lib.bp_pattern(sp, ns, dp, nd, nvec, chunk_vecs, mode, out_mult, sink.data_ptr(), stream)
+            rc = self.lib.bp_pattern(sp, ns, dp, nd, nvec, chunk_vecs, mode, out_mult, self.sink.data_ptr(),
+                                     self.stream)
             if rc != 0:
                 raise RuntimeError(f"bp_pattern returned {rc}")
         return run
 
-    def compare(label, entries):
-        """entries: (name, launch, bytes per launch); rounds alternate over the entries."""
+    def entries(self, w):
+        """(name, launch, bytes per launch) of a workload's dominant kernel, its pattern and the pattern's
+        reads alone; None for workloads without a contiguous twin."""
+        if isinstance(w, AllReduceWorkload) and w.algo == "fused":
+            nv = w.S * (2 if w.dtype_storage == "bf16" else 4) // 16
+            return [("library fused all-reduce", w.step, w.bytes_per_step),
+                    (f"pattern {w.N} in : {w.N} out", self.pattern(w.sets, nv), w.bytes_per_step),
+                    (f"pattern {w.N} in, no stores", self.pattern([(s, []) for s, _ in w.sets], nv),
+                     w.bytes_per_step // 2)]
+        if isinstance(w, HierWorkload):
+            nv = w.count * 2 // 16
+            return [("library two-level all-reduce", w.step, w.bytes_per_step),
+                    ("pattern 16 in : 16 out", self.pattern([(w.send, w.recv)], nv), w.bytes_per_step),
+                    ("pattern 16 in, no stores", self.pattern([(w.send, [])], nv), w.bytes_per_step // 2)]
+        if isinstance(w, FsdpWorkload):
+            nv, cv = w.S * 2 // 16, w.rc * 2 // 16
+            return [("library reduce-scatter bf16 -> fp32", w.dominant_launch, w.rs_bytes),
+                    ("pattern 64 in : owner's 2x out", self.pattern([(w.grads, w.gshards)], nv, cv, 1, 2), w.rs_bytes),
+                    ("pattern 64 in, no stores", self.pattern([(w.grads, [])], nv), w.N * w.S * 2)]
+        if isinstance(w, HsdpWorkload):
+            nv, cv = w.S * 2 // 16, w.rc * 2 // 16
+            return [("library HSDP reduce-scatter bf16 -> fp32", lambda _k: w.rs(), w.rs_bytes),
+                    ("pattern 16 in : both holders' 2x out", self.pattern([(w.grads, w.gshards)], nv, cv, 1, 2),
+                     w.rs_bytes),
+                    ("pattern 16 in, no stores", self.pattern([(w.grads, [])], nv), w.N * w.S * 2)]
+        return None
+
+    @staticmethod
+    def compare(label, entries, rounds=3, steps=20, warm=3):
+        """Time every entry, alternating over rounds; medians with min and max."""
+        import statistics
         rates = {name: [] for name, _, _ in entries}
         for _ in range(rounds):
             for name, fn, nbytes in entries:
@@ -1079,8 +1113,30 @@ def run_patterns(args):
             med = statistics.median(r)
             out["rows"].append({"kernel": name, "GBps": round(med, 1), "min": round(min(r), 1),
                                 "max": round(max(r), 1), "us": round(nbytes / med / 1e3, 1), "bytes": nbytes})
-        print(json.dumps(out), flush=True)
         return out
+
+    def beside(self, w):
+        """The short form for the bench line: the dominant kernel and its pattern on the same buffers
+        (2 alternating rounds of 10 launches), or None."""
+        e = self.entries(w)
+        if e is None or e[0][2] < (1 << 28):    # a few-microsecond launch times the host loop, not the kernel
+            return None
+        c = self.compare(w.name, e[:2], rounds=2, steps=10, warm=2)
+        lib_r, pat_r = c["rows"]
+        return {"pattern": pat_r["kernel"], "pattern_GBps": pat_r["GBps"], "kernel_GBps": lib_r["GBps"],
+                "frac_of_pattern": round(lib_r["GBps"] / pat_r["GBps"], 4),
+                "what": "the dominant kernel and an unordered kernel moving the same bytes in the same tiles "
+                        "(bench_patterns.hip), timed alternately on the same buffers"}
+
+
+def run_patterns(args):
+    """Each dominant kernel against the access-pattern kernels on the same buffers, in
+    one process, alternating over rounds: the gap between the two is what the kernel
+    itself costs.  Also reads alone, writes alone and a 1 : 1 copy on two 2 GiB buffers."""
+    import gc as pygc
+    import torch
+    P = Patterns()
+    gc = P.gc
 
     def release():
         pygc.collect()
@@ -1103,53 +1159,24 @@ def run_patterns(args):
 
     def lib_copy(_k):
         gc.gc_all_to_all([a_], [b_], [[[1]]], n)
-    results.append(compare("2 GiB streams (one allocation each)", [
+    results.append(P.compare("2 GiB streams (one allocation each)", [
         ("library segment copy (device-scope stores)", lib_copy, 2 * n),
-        ("pattern copy 1 in : 1 out", pattern([([a_], [b_])], nvec), 2 * n),
-        ("pattern reads alone", pattern([([a_], [])], nvec), n),
-        ("pattern writes alone", pattern([([], [b_])], nvec), n)]))
+        ("pattern copy 1 in : 1 out", P.pattern([([a_], [b_])], nvec), 2 * n),
+        ("pattern reads alone", P.pattern([([a_], [])], nvec), n),
+        ("pattern writes alone", P.pattern([([], [b_])], nvec), n)]))
+    print(json.dumps(results[-1]), flush=True)
     del a_, b_
     release()
 
-    for layout in ("arena", "separate"):
-        w = make(ns(workload="ar_bf16_n8", layout=layout))
-        nv = w.S * 2 // 16
-        results.append(compare(f"ar_bf16_n8 ({w.layout})", [
-            ("library fused all-reduce", w.step, w.bytes_per_step),
-            ("pattern 8 in : 8 out", pattern(w.sets, nv), w.bytes_per_step),
-            ("pattern 8 in, no stores", pattern([(s, []) for s, _ in w.sets], nv), w.bytes_per_step // 2)]))
+    for name, layout in (("ar_bf16_n8", "arena"), ("ar_bf16_n8", "separate"), ("hier_ar_n16", "arena"),
+                         ("fsdp_layer_n64", "arena"), ("hsdp_layer_n16", "arena")):
+        w = make(ns(workload=name, layout=layout))
+        label = f"{name} ({w.layout})" if name.startswith(("ar_", "hier")) else f"{name} reduce-scatter ({w.layout})"
+        results.append(P.compare(label, P.entries(w)))
+        print(json.dumps(results[-1]), flush=True)
         del w
         release()
-
-    w = make(ns(workload="hier_ar_n16"))
-    nv = w.count * 2 // 16
-    results.append(compare(f"hier_ar_n16 ({w.layout})", [
-        ("library two-level all-reduce", w.step, w.bytes_per_step),
-        ("pattern 16 in : 16 out", pattern([(w.send, w.recv)], nv), w.bytes_per_step),
-        ("pattern 16 in, no stores", pattern([(w.send, [])], nv), w.bytes_per_step // 2)]))
-    del w
-    release()
-
-    w = make(ns(workload="fsdp_layer_n64"))
-    nv, cv = w.S * 2 // 16, w.rc * 2 // 16
-    rd = w.N * w.S * 2
-    results.append(compare(f"fsdp_layer_n64 reduce-scatter ({w.layout})", [
-        ("library reduce-scatter bf16 -> fp32", w.dominant_launch, w.rs_bytes),
-        ("pattern 64 in : owner's 2x out", pattern([(w.grads, w.gshards)], nv, cv, 1, 2), w.rs_bytes),
-        ("pattern 64 in, no stores", pattern([(w.grads, [])], nv), rd)]))
-    del w
-    release()
-
-    w = make(ns(workload="hsdp_layer_n16"))
-    nv, cv = w.S * 2 // 16, w.rc * 2 // 16
-    rd = w.N * w.S * 2
-    results.append(compare(f"hsdp_layer_n16 reduce-scatter ({w.layout})", [
-        ("library HSDP reduce-scatter bf16 -> fp32", lambda _k: w.rs(), w.rs_bytes),
-        ("pattern 16 in : both holders' 2x out", pattern([(w.grads, w.gshards)], nv, cv, 1, 2), w.rs_bytes),
-        ("pattern 16 in, no stores", pattern([(w.grads, [])], nv), rd)]))
-    del w
-    release()
-    print(json.dumps({"patterns": results, "rounds": rounds, "steps": steps, "warmup": warm}), flush=True)
+    print(json.dumps({"patterns": results, "rounds": 3, "steps": 20, "warmup": 3}), flush=True)
 
 
 def main():
@@ -1200,6 +1227,10 @@ def main():
             out["allreduce_in_step"] = {
                 "ms_per_step": round(ar, 4), "value": round(w.dominant_bytes / (ar * 1e-3) / 1e9, 2),
                 "unit": "GB/s (algorithmic: part of each freshly packed bucket is served by the 256 MB MALL)"}
+    if not args.no_extras:
+        side = Patterns().beside(w)
+        if side is not None:
+            out["pattern"] = side
     if not args.no_copy_ceiling:
         ceiling = copy_ceiling()
         out["copy_ceiling"] = {"value": round(ceiling, 2), "unit": "GB/s",
