@@ -996,7 +996,7 @@ def run_extras(args):
     import gc as pygc
     import torch
     out = {}
-    pats = Patterns()
+    pats = Patterns.optional()
     for key, name, layout, steps, warmup in EXTRAS:
         a = argparse.Namespace(**vars(args))
         a.workload, a.layout, a.algo, a.order, a.stagger = name, layout, "fused", "ring", None
@@ -1021,7 +1021,7 @@ def run_extras(args):
                 "ms_per_step": round(ar, 4), "value": round(w.dominant_bytes / (ar * 1e-3) / 1e9, 2),
                 "unit": "GB/s (algorithmic: part of each freshly packed bucket is served by the 256 MB MALL)"}
             line["roofline"]["note"] = "the 226 bucket all-reduces launched alone (no pack before them): HBM-bound"
-        side = pats.beside(w)
+        side = pats.beside(w) if pats is not None else None
         if side is not None:
             line["pattern"] = side
         if not args.no_cpu and layout == "arena":
@@ -1056,6 +1056,15 @@ class Patterns:
                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         self.sink = torch.zeros(256, dtype=torch.int32, device="cuda")
         self.stream = torch.cuda.current_stream().cuda_stream
+
+    @classmethod
+    def optional(cls):
+        """The pattern kernels for the bench line's `pattern` keys, or None (with a note) if they are not
+        built: the keys are context, the measurement does not depend on them."""
+        if not os.path.exists(os.path.join(ROOT, "libbenchpatterns.so")):
+            print("libbenchpatterns.so is not built: the bench line carries no pattern keys", file=sys.stderr)
+            return None
+        return cls()
 
     def pattern(self, sets, nvec, chunk_vecs=0, mode=0, out_mult=1):
         """A launch of the pattern over sets, a list of (sources, destinations) tensor lists rotated over the steps."""
@@ -1227,8 +1236,9 @@ def main():
             out["allreduce_in_step"] = {
                 "ms_per_step": round(ar, 4), "value": round(w.dominant_bytes / (ar * 1e-3) / 1e9, 2),
                 "unit": "GB/s (algorithmic: part of each freshly packed bucket is served by the 256 MB MALL)"}
-    if not args.no_extras:
-        side = Patterns().beside(w)
+    pats = Patterns.optional() if not args.no_extras else None
+    if pats is not None:
+        side = pats.beside(w)
         if side is not None:
             out["pattern"] = side
     if not args.no_copy_ceiling:
