@@ -56,3 +56,17 @@ def test_pattern_kernel_refuses_bad_arguments():
     mis = (ctypes.c_void_p * 2)(0x10000, 0x10008)  # second source not 16-byte aligned
     assert lib.bp_pattern(mis, 2, arr, 1, 64, 0, 0, 1, sink, None) == 1
     assert lib.bp_pattern(arr, 1, arr, 1, 64, 0, 0, 1, None, None) == 1   # no sink
+
+
+def test_committed_profiles_match_the_kernel_sources():
+    """Every workload's committed rocprofv3 summary was taken on the current sources of its dominant
+    kernel (so bench.py reports its HBM traffic rather than null), and that traffic is the algorithmic
+    bytes within 1 %: no kernel re-reads or over-fetches."""
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    for workload in bench.WORKLOAD_KERNELS:
+        assert bench.traffic_from_profiles(workload) is not None, f"{workload}: profile taken on other sources"
+        text = open(os.path.join(ROOT, "profiles", f"{workload}_profile.md"), encoding="utf-8").read()
+        ratio = float(re.search(r"traffic_over_algorithmic:\s*([0-9.]+)", text).group(1))
+        assert 0.99 <= ratio <= 1.01, (workload, ratio)
