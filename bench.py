@@ -1241,6 +1241,13 @@ def main():
         side = pats.beside(w)
         if side is not None:
             out["pattern"] = side
+    if not args.no_extras and isinstance(w, AllReduceWorkload):
+        # the same steps captured in one HIP graph and replayed: the kernel back to back with no
+        # host work between launches (the eager loop adds the launch gap to every step)
+        n = 4 * len(w.ptrs)
+        g_us = graph_us(w.step, n)
+        out["graph"] = {"us_per_step": round(g_us, 3), "value": round(w.bytes_per_step / (g_us * 1e-6) / 1e9, 2),
+                        "launches_per_replay": n}
     if not args.no_copy_ceiling:
         ceiling = copy_ceiling()
         out["copy_ceiling"] = {"value": round(ceiling, 2), "unit": "GB/s",
